@@ -1,0 +1,2 @@
+"""CPU fp64 oracle (test infrastructure only; see mla_oracle)."""
+from .mla_oracle import *  # noqa: F401,F403
