@@ -1,0 +1,212 @@
+#!/usr/bin/env python3
+"""Throughput benchmark of the sparse MLA paged decode on one MI355X.
+
+A step is one call of mla_sparse_decode (index resolution, gather, dequant,
+QK^T, online softmax, PV, epilogue and -- when the plan splits the top-k
+list -- the LSE combine) over one batch of synthetic input already resident
+in HBM.  Steps rotate over several input sets (same cache pool, different Q
+and index lists) so the bytes touched per rotation exceed the 256 MB
+Infinity Cache; timing uses HIP events on the launch stream.
+
+Prints one JSON line on stdout.  Default workload: B=64, topk=512, 64 heads,
+65,536-token sequences over a 16,384-page pool with 1% outlier channels.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E peak
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16/fp16 MFMA peak
+FLOP_PER_TOKEN = 2 * 64 * 512 + 2 * 64 * 448   # QK^T + PV per valid (query, token)
+Q_BYTES = 64 * 512 * 2
+OUT_BYTES = 64 * 448 * 2 + 64 * 4
+TOKEN_BYTES = 584
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def workload_stats(w):
+    """Valid entries, attended count and algorithmic bytes of one step."""
+    lens = w.seq_lens.astype(np.int64)[:, None]
+    idx = w.topk_idx.astype(np.int64)
+    valid = (idx >= 0) & (idx < lens)
+    n_valid = int(valid.sum())
+    pages = set()
+    for b in range(w.batch):
+        lp = np.unique(idx[b][valid[b]] // 256)
+        pages.update((b, int(p)) for p in lp)
+    byts = (w.batch * (Q_BYTES + OUT_BYTES + 4) + TOKEN_BYTES * n_valid + 4 * w.batch * w.topk
+            + 4 * len(pages))
+    return dict(n_valid=n_valid, attended=64 * n_valid, bytes=byts, kv_bytes=TOKEN_BYTES * n_valid,
+                flops=FLOP_PER_TOKEN * n_valid)
+
+
+def cpu_baseline(w, seconds):
+    """Time the fp64 CPU oracle on passes over the same workload (set 0)."""
+    from oracle.mla_oracle import sparse_mla_decode as oracle_decode
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+                      or [1])
+    except Exception:  # threadpoolctl missing: report the process's CPU affinity
+        threads = len(os.sched_getaffinity(0))
+    st = workload_stats(w)
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        oracle_decode(w.q_bits, w.kv_pages, w.page_table, w.topk_idx, w.seq_lens, w.softmax_scale)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or passes >= 1000:
+            break
+    return {"value": st["attended"] * passes / el, "unit": "attended (query*head*token)/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"{passes} full pass(es) of the timed workload's first input set "
+                      f"({w.batch} queries, {st['n_valid']} valid entries) in {el:.1f} s; "
+                      f"numpy float64 with {threads} BLAS thread(s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=3, help="workload index 0..4")
+    ap.add_argument("--nsplit", type=int, default=0, help="force top-k slices per query (0 = plan)")
+    ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = enough to exceed MALL)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="per-launch HBM bytes measured with rocprofv3 counters")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_mla_decode_page_amd as mlasd
+    from gen.synth import CONFIG_NAMES, make_config, rotation_sets
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    mlasd.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t0 = time.perf_counter()
+    w = make_config(args.config)
+    st = workload_stats(w)
+    n_sets = args.sets or int(min(64, max(1, math.ceil(640e6 / st["bytes"]))))
+    sets = rotation_sets(w, n_sets, seed=777 + args.config)
+    log(f"workload {CONFIG_NAMES[args.config]}: {n_sets} input sets built in {time.perf_counter() - t0:.1f} s")
+
+    kv = torch.from_numpy(w.kv_pages).to(dev)
+    pt = torch.from_numpy(w.page_table).to(dev)
+    lens = torch.from_numpy(w.seq_lens).to(dev)
+    dsets = []
+    for s in sets:
+        dsets.append(dict(
+            q=torch.from_numpy(s.q_bits.view(np.int16)).view(torch.bfloat16).to(dev),
+            idx=torch.from_numpy(s.topk_idx).to(dev),
+            out=torch.empty((w.batch, 64, 448), dtype=torch.bfloat16, device=dev),
+            lse=torch.empty((w.batch, 64), dtype=torch.float32, device=dev)))
+    stats = [workload_stats(s) for s in sets]
+    nsplit, split_len = mlasd.plan(w.batch, w.topk, args.nsplit)
+    stream = torch.cuda.current_stream(dev)
+    nsplit_arg = args.nsplit if args.nsplit > 0 else None
+
+    def step(i):
+        d = dsets[i % n_sets]
+        mlasd.mla_sparse_decode(d["q"], kv, pt, d["idx"], lens, w.softmax_scale, out=d["out"],
+                                lse=d["lse"], stream=stream, nsplit=nsplit_arg)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize(dev)
+    if not all(torch.isfinite(d["lse"]).any().item() for d in dsets[:min(n_sets, args.warmup)]):
+        raise RuntimeError("non-finite output in warmup")
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    ev1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+
+    order = [(args.warmup + i) % n_sets for i in range(args.steps)]
+    attended = sum(stats[k]["attended"] for k in order) / args.steps
+    byts = sum(stats[k]["bytes"] for k in order) / args.steps
+    kvb = sum(stats[k]["kv_bytes"] for k in order) / args.steps
+    flops = sum(stats[k]["flops"] for k in order) / args.steps
+    sec = ms_step / 1e3
+    achieved = byts / sec / 1e9
+
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            tj = json.load(open(args.traffic_json))
+            key = f"config{args.config}_nsplit{nsplit}"
+            if key in tj:
+                traffic = tj[key]["bytes_per_launch"]
+        except Exception:
+            traffic = None
+
+    res = {
+        "metric": "sparse-MLA decode: attended (query*head*token)/s + achieved HBM GB/s vs peak",
+        "value": attended / sec,
+        "unit": "attended (query*head*token)/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": CONFIG_NAMES[args.config],
+            "batch": w.batch, "heads": 64, "topk": w.topk,
+            "valid_entries_per_step": stats[0]["n_valid"],
+            "nsplit": nsplit, "split_len": split_len, "input_sets": n_sets,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_step": byts,
+            "kv_gbs": kvb / sec / 1e9,
+            "mfma_tflops": flops / sec / 1e12,
+            "mfma_frac": flops / sec / 1e12 / BF16_PEAK_TFLOPS,
+            "timed": "decode kernel" + (" + LSE combine kernel" if nsplit > 1 else ""),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

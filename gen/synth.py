@@ -300,3 +300,44 @@ def extra_index_set(w: Workload, seed):
                          outlier_channels=w.meta.get("outlier_channels"))
     out.meta["config_index"] = w.meta.get("config_index")
     return out
+
+
+def rotation_sets(w: Workload, n_sets, seed):
+    """n_sets - 1 further (Q, index list) sets on the pool of `w` for timing
+    runs whose working set must exceed the caches.  Each set draws a new Q
+    and new distinct positions per query (same lengths and -1 padding rule);
+    the record bytes written at a newly selected slot are copied from a
+    record that `w` already selected (same value distribution, no new draws),
+    so only addresses change between sets.  Returns [w, set1, ...]."""
+    rng = _rng(seed)
+    flat = w.kv_pages.reshape(-1)
+    bb, jj = np.nonzero(w.topk_idx >= 0)
+    pos0 = w.topk_idx[bb, jj].astype(np.int64)
+    src_pg = w.page_table[bb, pos0 // PAGE_TOKENS].astype(np.int64)
+    src_sl = pos0 % PAGE_TOKENS
+    src_rec = flat[(src_pg * PAGE_BYTES + src_sl * TOKEN_BYTES)[:, None] + np.arange(TOKEN_BYTES)]
+    src_sc = flat[(src_pg * PAGE_BYTES + SCALE_BASE + src_sl * SCALE_BYTES)[:, None] + np.arange(SCALE_BYTES)]
+    out = [w]
+    B, K = w.topk_idx.shape
+    lens = w.seq_lens.astype(np.int64)
+    for _ in range(n_sets - 1):
+        idx = np.full((B, K), -1, dtype=np.int32)
+        for b in range(B):
+            L = int(lens[b])
+            if L >= K:
+                idx[b] = rng.choice(L, size=K, replace=False)
+            elif L > 0:
+                idx[b, :L] = rng.permutation(L)
+        q_bits = bf16_bits(rng.standard_normal((B, HEADS, D_QK)))
+        nb, nj = np.nonzero(idx >= 0)
+        pos = idx[nb, nj].astype(np.int64)
+        pg = w.page_table[nb, pos // PAGE_TOKENS].astype(np.int64)
+        sl = pos % PAGE_TOKENS
+        pick = rng.integers(0, len(src_rec), size=len(pos)) if len(src_rec) else np.zeros(0, np.int64)
+        if len(pos) and len(src_rec):
+            flat[(pg * PAGE_BYTES + sl * TOKEN_BYTES)[:, None] + np.arange(TOKEN_BYTES)] = src_rec[pick]
+            flat[(pg * PAGE_BYTES + SCALE_BASE + sl * SCALE_BYTES)[:, None] + np.arange(SCALE_BYTES)] = src_sc[pick]
+        out.append(Workload(name=w.name, q_bits=q_bits, kv_pages=w.kv_pages, page_table=w.page_table,
+                            topk_idx=idx, seq_lens=w.seq_lens, softmax_scale=w.softmax_scale,
+                            meta=dict(w.meta, rotation=True)))
+    return out

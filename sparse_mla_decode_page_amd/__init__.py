@@ -1,0 +1,17 @@
+"""Sparse MLA paged decode for MI355X (gfx950): Python binding of libmlasd.
+
+The decode runs in hand-written HIP kernels behind a C ABI
+(include/mlasd.h); this package only marshals torch tensors to it.
+"""
+from ._binding import (  # noqa: F401
+    MlasdError,
+    library_path,
+    load_library,
+    mla_sparse_decode,
+    mla_sparse_gather_dequant,
+    plan,
+    status_string,
+)
+
+__all__ = ["mla_sparse_decode", "mla_sparse_gather_dequant", "plan", "load_library",
+           "library_path", "status_string", "MlasdError"]

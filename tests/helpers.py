@@ -1,0 +1,40 @@
+"""Shared test helpers: device upload, tolerance checks, page-style report."""
+import numpy as np
+import torch
+
+# Tolerances for the attention outputs (bf16 out vs fp64 oracle): elementwise
+# |d| <= 2e-3 + 1e-2 * |ref| for out, |d| <= 1e-3 for lse.
+OUT_ATOL = 2e-3
+OUT_RTOL = 1e-2
+LSE_ATOL = 1e-3
+
+
+def to_device(w, device="cuda"):
+    return dict(
+        q=torch.from_numpy(w.q_bits.view(np.int16)).view(torch.bfloat16).to(device),
+        kv_pages=torch.from_numpy(w.kv_pages).to(device),
+        page_table=torch.from_numpy(w.page_table).to(device),
+        topk_idx=torch.from_numpy(w.topk_idx).to(device),
+        seq_lens=torch.from_numpy(w.seq_lens).to(device),
+    )
+
+
+def check_attention(out, lse, ref_out, ref_lse, label=""):
+    """Elementwise comparison; returns the pages-style report line."""
+    o = out.float().cpu().double().numpy()
+    l = lse.cpu().double().numpy()
+    assert o.shape == ref_out.shape and l.shape == ref_lse.shape
+    d = np.abs(o - ref_out)
+    bad = ~(d <= OUT_ATOL + OUT_RTOL * np.abs(ref_out))
+    n_bad = int(bad.sum())
+    inf_ref = np.isneginf(ref_lse)
+    assert np.array_equal(np.isneginf(l), inf_ref), f"{label}: -inf lse pattern differs"
+    dl = np.abs(l[~inf_ref] - ref_lse[~inf_ref]) if (~inf_ref).any() else np.zeros(1)
+    maxref = np.abs(ref_out).max() if ref_out.size else 0.0
+    line = (f"{label}: out max|d|={d.max() if d.size else 0:.3e} mean={d.mean() if d.size else 0:.3e} "
+            f"rel={(d.max() / maxref) if maxref > 0 else 0:.3e} | lse max|d|={dl.max():.3e} | "
+            f"outside tol: {n_bad}/{d.size}")
+    print(line, flush=True)
+    assert n_bad == 0, line
+    assert dl.max() <= LSE_ATOL, line
+    return line

@@ -1,0 +1,243 @@
+"""Parity of the HIP path (through the C ABI) with the CPU fp64 oracle.
+
+Gather + dequant must match bit for bit; attention outputs within
+|d| <= 2e-3 + 1e-2 |ref| (out) and |d| <= 1e-3 (lse)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import sparse_mla_decode_page_amd as mlasd
+from gen import synth as G
+from oracle import mla_oracle as O
+
+from helpers import check_attention, to_device
+
+pytestmark = pytest.mark.gpu
+
+_CONFIG_CACHE = {}
+
+
+def config(i):
+    if i not in _CONFIG_CACHE:
+        w = G.make_config(i)
+        ref = O.sparse_mla_decode(w.q_bits, w.kv_pages, w.page_table, w.topk_idx, w.seq_lens,
+                                  w.softmax_scale)
+        _CONFIG_CACHE[i] = (w, ref)
+    return _CONFIG_CACHE[i]
+
+
+def run(w, nsplit=None, stream=None):
+    d = to_device(w)
+    out, lse = mlasd.mla_sparse_decode(d["q"], d["kv_pages"], d["page_table"], d["topk_idx"],
+                                       d["seq_lens"], w.softmax_scale, nsplit=nsplit, stream=stream)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _bf16_to_f64(t):
+    return t.float().cpu().double().numpy()
+
+
+# ----------------------------------------------------------------------------
+# gather / dequant: bit-exact
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("i", [0, 1, 2, 3, 4])
+def test_gather_dequant_bit_exact(i):
+    w, _ = config(i)
+    print(f"gather config {i}", flush=True)
+    d = to_device(w)
+    k, v, valid = mlasd.mla_sparse_gather_dequant(d["kv_pages"], d["page_table"], d["topk_idx"],
+                                                  d["seq_lens"])
+    torch.cuda.synchronize()
+    rows, ok = O.gather_dequant(w.kv_pages, w.page_table, w.topk_idx, w.seq_lens)
+    assert np.array_equal(valid.cpu().numpy().astype(bool), ok)
+    kk = _bf16_to_f64(k)
+    vv = v.float().cpu().double().numpy()
+    assert np.array_equal(kk, rows), np.argwhere(kk != rows)[:5]
+    assert np.array_equal(vv, rows[..., :448]), np.argwhere(vv != rows[..., :448])[:5]
+
+
+def _all_codes_pool(scale_bytes):
+    """Two pages; slot s of the token sequence uses nope bytes (d + 37*s) % 256
+    (every fp8 code, including the NaN codes) and scale byte scale_bytes[s % n]
+    in every group."""
+    rng = np.random.default_rng(11)
+    pool = np.full((2, 149504), 0x7F, dtype=np.uint8)
+    flat = pool.reshape(-1)
+    for pos in range(512):
+        pg, sl = pos // 256, pos % 256
+        base = pg * 149504 + sl * 576
+        flat[base:base + 448] = (np.arange(448) + 37 * pos) % 256
+        flat[base + 448:base + 576] = G.bf16_bits(rng.standard_normal(64)).view(np.uint8)
+        sbase = pg * 149504 + 147456 + sl * 8
+        flat[sbase:sbase + 7] = scale_bytes[pos % len(scale_bytes)]
+        flat[sbase + 7] = 0xEE
+    return pool
+
+
+@pytest.mark.parametrize("scale_bytes,check_v", [
+    ([112, 115, 120, 125, 127, 130, 134], True),          # fp16 V exact range
+    ([10, 50, 100, 111, 135, 140, 200, 245], False),      # bf16 K only
+    ([0, 1, 5, 9], False),                                # results in bf16 subnormal range
+])
+def test_gather_dequant_all_codes(scale_bytes, check_v):
+    pool = _all_codes_pool(scale_bytes)
+    pt = np.array([[0, 1]], dtype=np.int32)
+    idx = np.arange(512, dtype=np.int32)[None][:, ::-1].copy()
+    lens = np.array([512], dtype=np.int32)
+    dev = lambda a: torch.from_numpy(a).cuda()
+    k, v, valid = mlasd.mla_sparse_gather_dequant(dev(pool), dev(pt), dev(idx), dev(lens))
+    torch.cuda.synchronize()
+    rows, ok = O.gather_dequant(pool, pt, idx, lens)
+    assert ok.all() and valid.cpu().numpy().all()
+    kk = _bf16_to_f64(k)
+    nan = np.isnan(rows)
+    assert np.array_equal(np.isnan(kk), nan)
+    assert np.array_equal(kk[~nan], rows[~nan])
+    if check_v:
+        vv = v.float().cpu().double().numpy()
+        r = rows[..., :448]
+        assert np.array_equal(np.isnan(vv), np.isnan(r))
+        assert np.array_equal(vv[~np.isnan(r)], r[~np.isnan(r)])
+
+
+# ----------------------------------------------------------------------------
+# attention parity
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("i", [0, 1, 2, 3, 4])
+def test_decode_matches_oracle(i):
+    w, (ref_out, ref_lse) = config(i)
+    print(f"decode config {i} plan={mlasd.plan(w.batch, w.topk)}", flush=True)
+    out, lse = run(w)
+    check_attention(out, lse, ref_out, ref_lse, label=f"config {i}")
+
+
+@pytest.mark.parametrize("i,nsplit", [(1, 1), (1, 2), (1, 4), (1, 16), (2, 1), (2, 3), (2, 16),
+                                      (3, 1), (3, 2), (3, 8), (4, 2), (4, 4)])
+def test_decode_forced_split(i, nsplit):
+    w, (ref_out, ref_lse) = config(i)
+    print(f"decode config {i} nsplit={nsplit}", flush=True)
+    out, lse = run(w, nsplit=nsplit)
+    check_attention(out, lse, ref_out, ref_lse, label=f"config {i} nsplit={nsplit}")
+
+
+def _custom(seed, lens, topk, **kw):
+    need = sum((L + 255) // 256 for L in lens)
+    return G.build_workload(seed, lens, topk, num_pages=need + 2, **kw)
+
+
+def _check_custom(w, nsplit=None, label=""):
+    ref_out, ref_lse = O.sparse_mla_decode(w.q_bits, w.kv_pages, w.page_table, w.topk_idx,
+                                           w.seq_lens, w.softmax_scale)
+    out, lse = run(w, nsplit=nsplit)
+    return check_attention(out, lse, ref_out, ref_lse, label=label)
+
+
+@pytest.mark.parametrize("topk", [1, 2, 31, 33, 45, 100, 257, 511])
+def test_ragged_topk(topk):
+    w = _custom(100 + topk, [3000, 700, 40000], topk)
+    for ns in (None, 1, 3):
+        _check_custom(w, nsplit=ns, label=f"topk={topk} nsplit={ns}")
+
+
+def test_topk1_returns_value_row():
+    w = _custom(5, [1000, 1], 1)
+    out, lse = run(w)
+    rows, ok = O.gather_dequant(w.kv_pages, w.page_table, w.topk_idx, w.seq_lens)
+    for b in range(w.batch):
+        exp_row = torch.from_numpy(rows[b, 0, :448]).to(torch.bfloat16).float().numpy()
+        assert np.array_equal(out[b].float().cpu().numpy(), np.broadcast_to(exp_row, (64, 448)))
+    _check_custom(w, label="topk=1")
+
+
+def test_masking_and_invalid_entries():
+    w = _custom(21, [5000, 300, 0, 2048], 64)
+    idx = w.topk_idx.copy()
+    # query 0: -1 at arbitrary positions, idx = len-1 and len, negatives, huge
+    idx[0, 3] = -1
+    idx[0, 10] = 4999
+    idx[0, 11] = 5000
+    idx[0, 12] = -123456
+    idx[0, 13] = 2 ** 31 - 1
+    idx[0, 40:] = -1
+    # query 3: valid positions whose page-table entries are out of range
+    w.page_table[3, 2] = -1
+    w.page_table[3, 5] = 10 ** 6
+    idx[3, :8] = [2 * 256 + 3, 5 * 256 + 7, 1, 2, 3, 4, 2 * 256 + 100, 5 * 256]
+    w.topk_idx = idx
+    for ns in (None, 1, 2):
+        _check_custom(w, nsplit=ns, label=f"masking nsplit={ns}")
+    out, lse = run(w)
+    assert np.all(out[2].float().cpu().numpy() == 0)
+    assert np.all(np.isneginf(lse[2].cpu().numpy()))
+
+
+def test_all_masked_and_empty():
+    w = _custom(3, [0, 0, 100], 32)
+    w.topk_idx[2] = -1
+    for ns in (None, 1):
+        out, lse = run(w, nsplit=ns)
+        assert np.all(out.float().cpu().numpy() == 0)
+        assert np.all(np.isneginf(lse.cpu().numpy()))
+
+
+def test_topk_zero_and_batch_zero():
+    w = _custom(4, [500, 20], 0)
+    out, lse = run(w)
+    assert np.all(out.float().cpu().numpy() == 0) and np.all(np.isneginf(lse.cpu().numpy()))
+    d = to_device(_custom(4, [500], 8))
+    e = {k: v[:0] for k, v in d.items() if k != "kv_pages"}
+    out, lse = mlasd.mla_sparse_decode(e["q"], d["kv_pages"], e["page_table"], e["topk_idx"],
+                                       e["seq_lens"], 0.1)
+    assert out.shape == (0, 64, 448) and lse.shape == (0, 64)
+
+
+def test_duplicates_count_each_time():
+    w = _custom(8, [3000], 40)
+    w.topk_idx[0, 20:30] = w.topk_idx[0, 0]
+    _check_custom(w, label="duplicates")
+
+
+def test_index_order_permutation():
+    w = _custom(9, [9000, 4000], 200)
+    base = _check_custom(w, label="order a")
+    w.topk_idx = w.topk_idx[:, np.random.default_rng(0).permutation(200)].copy()
+    _check_custom(w, label="order b")
+
+
+@pytest.mark.parametrize("scale", [0.0, 1.0 / math.sqrt(512), 0.25, -0.1])
+def test_softmax_scale_values(scale):
+    w = _custom(12, [2000, 6000], 128, softmax_scale=scale)
+    _check_custom(w, label=f"scale={scale}")
+
+
+def test_outliers_small_batch():
+    w = _custom(13, [65536, 65536], 512, outlier_frac=0.01)
+    for ns in (None, 1, 4):
+        _check_custom(w, nsplit=ns, label=f"outliers nsplit={ns}")
+
+
+def test_non_default_stream():
+    w, (ref_out, ref_lse) = config(2)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out, lse = run(w, stream=s)
+    s.synchronize()
+    check_attention(out, lse, ref_out, ref_lse, label="side stream")
+
+
+def test_repeat_calls_deterministic():
+    w, _ = config(3)
+    d = to_device(w)
+    outs = []
+    for _ in range(3):
+        o, l = mlasd.mla_sparse_decode(d["q"], d["kv_pages"], d["page_table"], d["topk_idx"],
+                                       d["seq_lens"], w.softmax_scale)
+        outs.append((o.clone(), l.clone()))
+    torch.cuda.synchronize()
+    for o, l in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
