@@ -37,8 +37,12 @@
  *     non-zero return nothing was enqueued (except MLASD_ERR_HIP, which
  *     reports a failed enqueue).  Data-dependent conditions (masked indices,
  *     out-of-range page ids) are not errors: such entries are skipped.
- *   - Calls on different streams may run concurrently; each call takes the
- *     split scratch it needs from the stream-ordered allocator of `stream`.
+ *   - Split scratch (fp32 partial outputs when a query's top-k list is cut
+ *     into slices) is owned by the library: one buffer per (device, stream),
+ *     grown with hipMalloc when a call needs more and kept until the process
+ *     ends.  Calls on different streams may run concurrently; calls on one
+ *     stream are ordered by the stream.  Growth synchronises the stream, so
+ *     under graph capture make a first call of the largest shape beforehand.
  */
 #ifndef MLASD_H
 #define MLASD_H

@@ -3,8 +3,10 @@
 
 #include <cmath>
 #include <cstdint>
+#include <map>
 #include <mutex>
 #include <string>
+#include <utility>
 
 #include "../../include/mlasd.h"
 #include "mlasd_internal.h"
@@ -37,6 +39,41 @@ int device_cus(int* cus) {
     cache[dev] = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
   }
   *cus = cache[dev];
+  return MLASD_OK;
+}
+
+// Split scratch: one buffer per (device, stream), grown on demand and kept
+// for the life of the process.  Growing synchronises that stream before the
+// old buffer is freed, so it must not happen during graph capture: a first
+// call with the largest shape outside capture sizes it.
+struct Workspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+int stream_workspace(hipStream_t stream, size_t bytes, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  Workspace& w = g_ws[{dev, stream}];
+  if (w.bytes < bytes) {
+    if (w.ptr) {
+      e = hipStreamSynchronize(stream);
+      if (e != hipSuccess) return hip_fail(e);
+      e = hipFree(w.ptr);
+      if (e != hipSuccess) return hip_fail(e);
+      w.ptr = nullptr;
+      w.bytes = 0;
+    }
+    const size_t want = (bytes + (1u << 20) - 1) & ~(size_t)((1u << 20) - 1);
+    e = hipMalloc(&w.ptr, want);
+    if (e != hipSuccess) return hip_fail(e);
+    w.bytes = want;
+  }
+  *out = w.ptr;
   return MLASD_OK;
 }
 
@@ -104,21 +141,17 @@ int decode_impl(const void* q, const void* kv_pages, int64_t num_pages, const in
   p.lse = lse;
   make_plan(batch, topk, nsplit_req, cus, &p.nsplit, &p.split_len);
 
-  void* scratch = nullptr;
   if (p.nsplit > 1) {
     const size_t n_o = (size_t)batch * p.nsplit * mlasd::kHeads * mlasd::kDV;
     const size_t n_l = (size_t)batch * p.nsplit * mlasd::kHeads;
-    hipError_t e = hipMallocAsync(&scratch, (n_o + n_l) * sizeof(float), stream);
-    if (e != hipSuccess) return hip_fail(e);
+    void* scratch = nullptr;
+    rc = stream_workspace(stream, (n_o + n_l) * sizeof(float), &scratch);
+    if (rc != MLASD_OK) return rc;
     p.part_o = (float*)scratch;
     p.part_lse = (float*)scratch + n_o;
   }
   hipError_t e = mlasd::launch_decode(p, stream);
   if (e == hipSuccess && p.nsplit > 1) e = mlasd::launch_combine(p, stream);
-  if (scratch) {
-    hipError_t ef = hipFreeAsync(scratch, stream);
-    if (e == hipSuccess) e = ef;
-  }
   if (e != hipSuccess) return hip_fail(e);
   return MLASD_OK;
 }
