@@ -1,0 +1,239 @@
+// C-ABI entry points: argument validation, split planning, scratch, launches.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "/root/repo/include/mlasd.h"
+#include "mlasd_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_fail(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return MLASD_ERR_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Compute-unit count of the current device, cached per device id.
+int device_cus(int* cus) {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= 64) return MLASD_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (std::string(prop.gcnArchName).rfind("gfx950", 0) != 0) return MLASD_ERR_DEVICE;
+    cache[dev] = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
+  }
+  *cus = cache[dev];
+  return MLASD_OK;
+}
+
+// Split scratch: one buffer per (device, stream), grown on demand and kept
+// for the life of the process.  Growing synchronises that stream before the
+// old buffer is freed, so it must not happen during graph capture: a first
+// call with the largest shape outside capture sizes it.
+struct Workspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+int stream_workspace(hipStream_t stream, size_t bytes, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  Workspace& w = g_ws[{dev, stream}];
+  if (w.bytes < bytes) {
+    if (w.ptr) {
+      e = hipStreamSynchronize(stream);
+      if (e != hipSuccess) return hip_fail(e);
+      e = hipFree(w.ptr);
+      if (e != hipSuccess) return hip_fail(e);
+      w.ptr = nullptr;
+      w.bytes = 0;
+    }
+    const size_t want = (bytes + (1u << 20) - 1) & ~(size_t)((1u << 20) - 1);
+    e = hipMalloc(&w.ptr, want);
+    if (e != hipSuccess) return hip_fail(e);
+    w.bytes = want;
+  }
+  *out = w.ptr;
+  return MLASD_OK;
+}
+
+// Split plan: one workgroup per (query, top-k slice).  Without a request the
+// slices are sized so the grid covers every compute unit once; a slice holds
+// a whole number of 32-token tiles.
+void make_plan(int32_t batch, int32_t topk, int32_t request, int cus, int32_t* nsplit,
+               int32_t* split_len) {
+  const int tile = mlasd::kTileTokens;
+  const int max_split = topk > 0 ? (topk + tile - 1) / tile : 1;
+  int ns;
+  if (request > 0) {
+    ns = request;
+  } else {
+    ns = batch > 0 ? (cus + batch - 1) / batch : 1;
+  }
+  if (ns > max_split) ns = max_split;
+  if (ns < 1) ns = 1;
+  int len = topk > 0 ? (topk + ns - 1) / ns : tile;
+  len = (len + tile - 1) / tile * tile;
+  ns = topk > 0 ? (topk + len - 1) / len : 1;
+  *nsplit = ns;
+  *split_len = len;
+}
+
+int check_common(const void* kv, int64_t num_pages, const int32_t* page_table, int32_t max_pages,
+                 const int32_t* topk_idx, int32_t topk, const int32_t* seq_lens, int32_t batch) {
+  if (batch < 0 || topk < 0 || topk > MLASD_MAX_TOPK) return MLASD_ERR_SHAPE;
+  if (batch == 0) return MLASD_OK;
+  if (num_pages < 1 || max_pages < 1) return MLASD_ERR_SHAPE;
+  if (!kv || !page_table || !seq_lens) return MLASD_ERR_NULL;
+  if (topk > 0 && !topk_idx) return MLASD_ERR_NULL;
+  if (!aligned(kv, 16) || !aligned(page_table, 4) || !aligned(seq_lens, 4) ||
+      (topk_idx && !aligned(topk_idx, 4)))
+    return MLASD_ERR_ALIGN;
+  return MLASD_OK;
+}
+
+int decode_impl(const void* q, const void* kv_pages, int64_t num_pages, const int32_t* page_table,
+                int32_t max_pages, const int32_t* topk_idx, int32_t topk, const int32_t* seq_lens,
+                int32_t batch, float softmax_scale, void* out, float* lse, int32_t nsplit_req,
+                hipStream_t stream) {
+  int rc = check_common(kv_pages, num_pages, page_table, max_pages, topk_idx, topk, seq_lens, batch);
+  if (rc != MLASD_OK) return rc;
+  if (!std::isfinite(softmax_scale)) return MLASD_ERR_VALUE;
+  if (batch == 0) return MLASD_OK;
+  if (!q || !out || !lse) return MLASD_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(out, 8) || !aligned(lse, 4)) return MLASD_ERR_ALIGN;
+  int cus = 0;
+  rc = device_cus(&cus);
+  if (rc != MLASD_OK) return rc;
+
+  mlasd::DecodeParams p{};
+  p.q = (const uint16_t*)q;
+  p.kv = (const uint8_t*)kv_pages;
+  p.num_pages = num_pages;
+  p.page_table = page_table;
+  p.max_pages = max_pages;
+  p.topk_idx = topk_idx;
+  p.topk = topk;
+  p.seq_lens = seq_lens;
+  p.batch = batch;
+  p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+  p.out = (uint16_t*)out;
+  p.lse = lse;
+  make_plan(batch, topk, nsplit_req, cus, &p.nsplit, &p.split_len);
+
+  if (p.nsplit > 1) {
+    const size_t n_o = (size_t)batch * p.nsplit * mlasd::kHeads * mlasd::kDV;
+    const size_t n_l = (size_t)batch * p.nsplit * mlasd::kHeads;
+    void* scratch = nullptr;
+    rc = stream_workspace(stream, (n_o + n_l) * sizeof(float), &scratch);
+    if (rc != MLASD_OK) return rc;
+    p.part_o = (float*)scratch;
+    p.part_lse = (float*)scratch + n_o;
+  }
+  hipError_t e = mlasd::launch_decode(p, stream);
+  if (e == hipSuccess && p.nsplit > 1) e = mlasd::launch_combine(p, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return MLASD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_sparse_decode(const void* q, const void* kv_pages, int64_t num_pages,
+                      const int32_t* page_table, int32_t max_pages, const int32_t* topk_idx,
+                      int32_t topk, const int32_t* seq_lens, int32_t batch, float softmax_scale,
+                      void* out, float* lse, mlasd_stream_t stream) {
+  return decode_impl(q, kv_pages, num_pages, page_table, max_pages, topk_idx, topk, seq_lens, batch,
+                     softmax_scale, out, lse, 0, (hipStream_t)stream);
+}
+
+int mla_sparse_decode_ex(const void* q, const void* kv_pages, int64_t num_pages,
+                         const int32_t* page_table, int32_t max_pages, const int32_t* topk_idx,
+                         int32_t topk, const int32_t* seq_lens, int32_t batch, float softmax_scale,
+                         void* out, float* lse, int32_t nsplit, mlasd_stream_t stream) {
+  return decode_impl(q, kv_pages, num_pages, page_table, max_pages, topk_idx, topk, seq_lens, batch,
+                     softmax_scale, out, lse, nsplit, (hipStream_t)stream);
+}
+
+int mla_sparse_plan(int32_t batch, int32_t topk, int32_t nsplit_request, int32_t num_cus,
+                    int32_t* nsplit, int32_t* split_len) {
+  if (!nsplit || !split_len) return MLASD_ERR_NULL;
+  if (batch < 0 || topk < 0 || topk > MLASD_MAX_TOPK) return MLASD_ERR_SHAPE;
+  int cus = num_cus;
+  if (cus <= 0) {
+    int rc = device_cus(&cus);
+    if (rc != MLASD_OK) return rc;
+  }
+  make_plan(batch, topk, nsplit_request, cus, nsplit, split_len);
+  return MLASD_OK;
+}
+
+int mla_sparse_gather_dequant(const void* kv_pages, int64_t num_pages, const int32_t* page_table,
+                              int32_t max_pages, const int32_t* topk_idx, int32_t topk,
+                              const int32_t* seq_lens, int32_t batch, void* k_rows, void* v_rows,
+                              uint8_t* valid, mlasd_stream_t stream) {
+  int rc = check_common(kv_pages, num_pages, page_table, max_pages, topk_idx, topk, seq_lens, batch);
+  if (rc != MLASD_OK) return rc;
+  if (batch == 0 || topk == 0) return MLASD_OK;
+  if (!k_rows || !v_rows || !valid) return MLASD_ERR_NULL;
+  if (!aligned(k_rows, 16) || !aligned(v_rows, 16)) return MLASD_ERR_ALIGN;
+  int cus = 0;
+  rc = device_cus(&cus);
+  if (rc != MLASD_OK) return rc;
+  mlasd::GatherParams p{};
+  p.kv = (const uint8_t*)kv_pages;
+  p.num_pages = num_pages;
+  p.page_table = page_table;
+  p.max_pages = max_pages;
+  p.topk_idx = topk_idx;
+  p.topk = topk;
+  p.seq_lens = seq_lens;
+  p.batch = batch;
+  p.k_rows = (uint16_t*)k_rows;
+  p.v_rows = (uint16_t*)v_rows;
+  p.valid = valid;
+  make_plan(batch, topk, 0, cus, &p.nsplit, &p.split_len);
+  hipError_t e = mlasd::launch_gather(p, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return MLASD_OK;
+}
+
+const char* mlasd_status_string(int status) {
+  switch (status) {
+    case MLASD_OK: return "ok";
+    case MLASD_ERR_NULL: return "null pointer argument";
+    case MLASD_ERR_SHAPE: return "size out of range";
+    case MLASD_ERR_ALIGN: return "misaligned pointer";
+    case MLASD_ERR_VALUE: return "invalid scalar argument";
+    case MLASD_ERR_HIP: return "HIP runtime error";
+    case MLASD_ERR_DEVICE: return "current device is not gfx950";
+    default: return "unknown status";
+  }
+}
+
+int mlasd_last_hip_error(void) { return g_last_hip_error; }
+
+const char* mlasd_version(void) { return "mlasd 0.1.0 (gfx950)"; }
+
+}  // extern "C"

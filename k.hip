@@ -1,0 +1,574 @@
+// gfx950 (CDNA4) kernels for sparse MLA decode over a paged FP8 KV cache.
+//
+// Method ("The Turning Point", "The Reasoning Process", Steps 3-5): one
+// program handles all heads of a query, so every selected KV row is fetched
+// once and Q K^T becomes a matrix product; the top-k list may be split over
+// several programs whose partial results are merged with the online-softmax
+// (log-sum-exp) rule.  Data flow per tile: gather -> dequantise -> concat
+// with rope -> Q K^T -> online softmax -> P V ("The Turning Point", "Output
+// Knowledge Created", item 2).  The 448 nope dims are not padded here: 448 is
+// a whole number of 32-wide MFMA K-steps, so the pages' pad-to-512 mask has
+// nothing to do on this hardware.
+//
+// Workgroup = (query b, slice s of its top-k list), 512 threads = 8 waves in
+// two roles, one wave of each role per SIMD, meeting at one barrier per
+// 32-token tile:
+//   consumers (waves 0..3): wave c owns heads [16c, 16c+16) and runs
+//       a4  S^T = K Q^T on v_mfma_f32_16x16x32_bf16, Q held in registers;
+//       a5  online softmax in fp32 (exp2 domain), one head per lane column;
+//       a6  O^T += V^T P^T on v_mfma_f32_16x16x32_f16 over all 448 dims, the
+//           V^T operand read with ds_read_b64_tr_b16 transposing loads;
+//       a7  epilogue: bf16 out + fp32 lse, or fp32 partials for the combine;
+//   producers (waves 4..7): wave p owns tokens [8p, 8p+8) of every tile and
+//       a2  gathers their records (576 B + 8 B scale record) into registers
+//           four tiles ahead, with loads whose issue never depends on data
+//           (masked slots read page 0, slot 0);
+//       a3  dequantises tile t+1 into the other LDS buffer (K bf16 token-major,
+//           V fp16 token-major with rows in PV k-slot order) while the
+//           consumers work on tile t.
+//   a1  before that, all waves validate, resolve through the page table and
+//       compact the slice's entries into an LDS list;
+//   a8  the combine kernel merges slices with the LSE rule.
+#include "mlasd_internal.h"
+
+namespace mlasd {
+__device__ unsigned long long g_tbuf[8192 * 40];
+__device__ int g_skip_partials = 0;
+#define TS(k) do { if ((threadIdx.x & 63) == 0 && blockIdx.x < 8192) g_tbuf[blockIdx.x * 40 + (k)] = wall_clock64(); } while (0)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = kThreads / 64;
+constexpr int kConsumers = 4;       // waves 0..3
+constexpr int kKRow = kDQK + 8;     // K tile row stride (bf16 elements), +16 B pad
+constexpr int kVRow = kDQK + 16;    // V tile row stride (fp16 elements): 448 dims, a
+                                    // 64-element spill area for lanes 56..63, +32 B pad
+constexpr int kDepth = 4;           // tiles gathered ahead by the producers
+constexpr int kTokPerProducer = kTileTokens / (kWaves - kConsumers);   // 8
+constexpr float kRescaleLog2 = 8.f; // lazy-rescale threshold (P <= 256)
+constexpr int kPvAhead = 3;         // PV operand blocks read ahead
+constexpr int kQkAhead = 2;         // QK^T operand k-steps read ahead
+
+struct __align__(16) Smem {
+  uint16_t k[2][kTileTokens * kKRow];   // 2 x 33,280 B
+  uint16_t v[2][kTileTokens * kVRow];   // 2 x 33,792 B
+  int32_t tok[kMaxTopk][2];             // compacted list: physical page, slot
+  uint16_t tok_entry[kMaxTopk];         //                 entry index in the slice
+  int32_t wave_cnt[kWaves];
+};
+
+// ---------------------------------------------------------------------------
+// small helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int logical_block(int n) {
+  // Workgroups are dispatched round-robin over the 8 XCDs (block i -> XCD
+  // i % 8).  Renumber so that consecutive logical blocks -- the slices of one
+  // query, which read the same Q -- run on the same XCD and share its L2.
+  const int i = blockIdx.x;
+  const int xcd = i & 7, k = i >> 3;
+  const int per = n >> 3, rem = n & 7;
+  return xcd < rem ? xcd * (per + 1) + k : rem * (per + 1) + (xcd - rem) * per + k;
+}
+
+template <typename V2>
+__device__ __forceinline__ uint32_t pack2(V2 v) {
+  static_assert(sizeof(V2) == 4, "two 16-bit lanes");
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  const bf16x2 r = {(__bf16)a, (__bf16)b};   // v_cvt_pk_bf16_f32, round to nearest even
+  return pack2(r);
+}
+
+// a1: one index entry -> (page, slot) if valid.  Validity: 0 <= p < seq_len,
+// logical page inside the page-table row, physical page inside the pool.
+__device__ __forceinline__ bool resolve_entry(int p, int seq_len, const int32_t* pt_row,
+                                              int32_t max_pages, int64_t num_pages,
+                                              int& page, int& slot) {
+  if (p < 0 || p >= seq_len) return false;
+  const int lp = p >> 8;
+  if (lp >= max_pages) return false;
+  const int pg = pt_row[lp];
+  if (pg < 0 || (int64_t)pg >= num_pages) return false;
+  page = pg;
+  slot = p & (kPageTokens - 1);
+  return true;
+}
+
+// a1 for a whole slice: validate, resolve and compact (stable order) the
+// n_ent <= 512 entries at `idx_row` into the LDS token list, one entry per
+// thread.  Returns the number of valid entries.  Ends with a barrier.
+__device__ int compact_slice(Smem& sm, const int32_t* idx_row, int n_ent, int seq_len,
+                             const int32_t* pt_row, int32_t max_pages, int64_t num_pages) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int p = tid < n_ent ? idx_row[tid] : -1;
+  int page = 0, slot = 0;
+  const bool v = resolve_entry(p, seq_len, pt_row, max_pages, num_pages, page, slot);
+  const uint64_t mask = __ballot(v);
+  const int in_wave = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+  if (lane == 0) sm.wave_cnt[wid] = __popcll(mask);
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int cnt = sm.wave_cnt[w];
+    before += (w < wid) ? cnt : 0;
+    total += cnt;
+  }
+  if (v) {
+    const int pos = before + in_wave;
+    sm.tok[pos][0] = page;
+    sm.tok[pos][1] = slot;
+    sm.tok_entry[pos] = (uint16_t)tid;
+  }
+  __syncthreads();
+  return total;
+}
+
+// PV k-slot of tile token t.  A consumer's S^T accumulator block mb holds
+// tokens 16mb + 4g + r in lane group g, row r; they feed k-slots 8g + 4mb + r
+// of the P^T operand, so the V tile stores token t in row slot_of(t).
+__device__ __forceinline__ int slot_of(int t) { return 8 * ((t >> 2) & 3) + 4 * (t >> 4) + (t & 3); }
+
+// a2 registers of one tile for one producer wave p: tokens 8p + j, j = 0..7.
+//   rec[j]: lanes 0..55 hold nope bytes [8 lane, 8 lane + 8) of token j,
+//           lanes 56..63 hold token j's 8-byte scale record;
+//   rope  : rope bytes [16 (lane & 7), +16) of token lane >> 3.
+// Record loads are buffer loads on a per-token descriptor spanning that
+// token's page; a tile position past the last valid entry gets a zero-size
+// descriptor, which returns zeros without touching memory, so prefetches
+// past the end of the slice cost nothing.  The rope load of such a position
+// re-reads the slice's last valid record (already cached); masked positions
+// get zero scores' weight either way.
+struct TileRegs {
+  u32x2 rec[kTokPerProducer];
+  u32x4 rope;
+};
+
+struct LastRecord {   // wave-uniform: the slice's last valid (page, slot)
+  int page, slot;
+};
+
+constexpr int kBufferDword3 = 0x00020000;   // raw buffer access, gfx9 family
+
+__device__ __forceinline__ void load_tile(TileRegs& r, const Smem& sm, const uint8_t* kv, int tile,
+                                          int n_valid, LastRecord last, int pw, int lane) {
+  const int c0 = tile * kTileTokens + kTokPerProducer * pw;
+  const int cc = min(c0, kMaxTopk - kTokPerProducer);
+#pragma unroll
+  for (int q = 0; q < kTokPerProducer / 2; ++q) {
+    const i32x4 t2 = *(const i32x4*)&sm.tok[cc + 2 * q][0];   // page, slot, page, slot
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int j = 2 * q + h;
+      const bool ok = c0 + j < n_valid;
+      // page and slot are the same in every lane: address math on the SALU
+      const int page = __builtin_amdgcn_readfirstlane(ok ? (h ? t2.z : t2.x) : 0);
+      const int slot = __builtin_amdgcn_readfirstlane(ok ? (h ? t2.w : t2.y) : 0);
+      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(kv + (int64_t)page * kPageBytes), (short)0, ok ? (int)kPageBytes : 0, kBufferDword3);
+      const int off = lane < 56 ? slot * kRecordBytes + 8 * lane : (int)kScaleBase + slot * kScaleRecordBytes;
+      r.rec[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rsrc, off, 0, 0));
+    }
+  }
+  {
+    const int j = lane >> 3;
+    const int ci = c0 + j;
+    int page = last.page, slot = last.slot;
+    if (ci < n_valid) {
+      page = sm.tok[ci][0];
+      slot = sm.tok[ci][1];
+    }
+    r.rope = *(const u32x4*)(kv + (int64_t)page * kPageBytes + slot * kRecordBytes + kDNope + 16 * (lane & 7));
+  }
+}
+
+// a3: dequantise one producer wave's 8 gathered tokens into LDS buffer `buf`.
+// Every lane stores 16 bytes per row at 16 * lane: lanes 0..55 hold dims
+// [8 lane, 8 lane + 8); lanes 56..63 (the scale-record lanes) land in the K
+// row's rope span, rewritten just after by the rope store, and in the V row's
+// spill area, which PV never reads.
+__device__ __forceinline__ void store_tile(Smem& sm, const TileRegs& r, int buf, int pw, int lane) {
+  const int g = lane >> 3;  // scale group of nope dims [8 lane, 8 lane + 8)
+  uint16_t* kb = &sm.k[buf][8 * lane];
+  uint16_t* vb = &sm.v[buf][8 * lane];
+#pragma unroll
+  for (int j = 0; j < kTokPerProducer; ++j) {
+    const uint32_t lo = __builtin_amdgcn_readlane(r.rec[j].x, 56);
+    const uint32_t hi = __builtin_amdgcn_readlane(r.rec[j].y, 56);
+    const uint32_t sb = ((g < 4) ? (lo >> (8 * g)) : (hi >> (8 * (g - 4)))) & 0xffu;
+    const float scale = __uint_as_float(sb << 23);   // 2^(sb-127) as an fp32 power of two
+    const uint32_t b0 = r.rec[j].x, b1 = r.rec[j].y;
+    u32x4 kq, vq;
+    kq.x = pack2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b0, scale, false));
+    kq.y = pack2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b0, scale, true));
+    kq.z = pack2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b1, scale, false));
+    kq.w = pack2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b1, scale, true));
+    vq.x = pack2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b0, scale, false));
+    vq.y = pack2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b0, scale, true));
+    vq.z = pack2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b1, scale, false));
+    vq.w = pack2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b1, scale, true));
+    const int t = kTokPerProducer * pw + j;
+    *(u32x4*)(kb + t * kKRow) = kq;
+    *(u32x4*)(vb + slot_of(t) * kVRow) = vq;
+  }
+  const int tr = kTokPerProducer * pw + (lane >> 3);
+  *(u32x4*)&sm.k[buf][tr * kKRow + kDNope + 8 * (lane & 7)] = r.rope;
+}
+
+// ---------------------------------------------------------------------------
+// a1-a7: main decode kernel
+// ---------------------------------------------------------------------------
+
+// A kernel argument read late in a long kernel is re-fetched from the
+// argument segment (a fresh memory round trip); pin what the epilogue needs
+// into scalar registers at entry instead.
+template <typename T>
+__device__ __forceinline__ T* pin_ptr(T* ptr) {
+  const uint64_t v = (uint64_t)ptr;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (T*)(((uint64_t)hi << 32) | lo);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeParams p_arg) {
+  __shared__ Smem sm;
+  DecodeParams p = p_arg;
+  p.out = pin_ptr(p_arg.out);
+  p.lse = pin_ptr(p_arg.lse);
+  p.part_o = pin_ptr(p_arg.part_o);
+  p.part_lse = pin_ptr(p_arg.part_lse);
+  p.nsplit = __builtin_amdgcn_readfirstlane(p_arg.nsplit);
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int blk = logical_block(p.batch * p.nsplit);
+  const int b = blk / p.nsplit, s = blk - b * p.nsplit;
+  const int e0 = s * p.split_len;
+  const int n_ent = max(0, min(p.topk - e0, p.split_len));
+  if (wid == 0) TS(0);
+
+  const int n_valid = compact_slice(sm, p.topk_idx + (int64_t)b * p.topk + e0, n_ent,
+                                    p.seq_lens[b], p.page_table + (int64_t)b * p.max_pages,
+                                    p.max_pages, p.num_pages);
+  const int ntiles = (n_valid + kTileTokens - 1) / kTileTokens;
+
+  if (wid == 0) TS(1);
+  // Both roles pass the same barriers: one after the first tile is stored,
+  // then one per tile.
+  if (wid >= kConsumers) {
+    // ---------------- producers: a2 + a3 ----------------
+    const int pw = wid - kConsumers;
+    if (ntiles == 0) {   // empty slice: nothing to gather
+      __syncthreads();
+      return;
+    }
+    const LastRecord last = {__builtin_amdgcn_readfirstlane(sm.tok[n_valid - 1][0]),
+                             __builtin_amdgcn_readfirstlane(sm.tok[n_valid - 1][1])};
+    TileRegs regs[kDepth];
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) load_tile(regs[u], sm, p.kv, u, n_valid, last, pw, lane);
+    store_tile(sm, regs[0], 0, pw, lane);
+    if (pw == 0) TS(2);
+    load_tile(regs[0], sm, p.kv, kDepth, n_valid, last, pw, lane);
+    __syncthreads();
+    for (int t0 = 0; t0 < ntiles; t0 += kDepth) {
+#pragma unroll
+      for (int u = 0; u < kDepth; ++u) {
+        const int t = t0 + u;
+        const int nxt = (u + 1) % kDepth;   // ring slot of tile t + 1
+        if (t + 1 < ntiles) store_tile(sm, regs[nxt], (t + 1) & 1, pw, lane);
+        if (t < 4) TS(16 + 4 * t + pw);
+        // issued on every path, so the loads in flight behind each ring slot
+        // are the same wherever it is consumed (past the end they re-read a
+        // cached record)
+        load_tile(regs[nxt], sm, p.kv, t + 1 + kDepth, n_valid, last, pw, lane);
+        if (t < ntiles) __syncthreads();
+      }
+    }
+    return;
+  }
+
+  // ---------------- consumers: a4 - a7 ----------------
+  const int g = lane >> 4;         // MFMA lane group
+  const int col = lane & 15;       // MFMA column: head within the wave's 16
+  const int head = 16 * wid + col;
+
+  // Q^T operand for the wave's 16 heads, kept in registers: dims [32k + 8g, +8).
+  bf16x8 qreg[16];
+  {
+    const uint16_t* qrow = p.q + ((int64_t)b * kHeads + head) * kDQK + 8 * g;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) qreg[k] = *(const bf16x8*)(qrow + 32 * k);
+  }
+  f32x4 oacc[28];
+#pragma unroll
+  for (int i = 0; i < 28; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  __syncthreads();
+  if (wid == 0) TS(3);
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    if (wid == 0 && t < 4) TS(4 + t);
+    // a4: S^T[token][head] for the tile's 32 tokens: two 16-token blocks,
+    // two accumulation chains each, operands read kQkAhead k-steps ahead.
+    const uint16_t* krow = &sm.k[buf][col * kKRow + 8 * g];
+    bf16x8 ka[kQkAhead + 1][2];
+#pragma unroll
+    for (int k = 0; k < kQkAhead; ++k)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) ka[k][mb] = *(const bf16x8*)(krow + 16 * mb * kKRow + 32 * k);
+    f32x4 sc[2][2] = {};
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if (k + kQkAhead < 16) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          ka[(k + kQkAhead) % (kQkAhead + 1)][mb] = *(const bf16x8*)(krow + 16 * mb * kKRow + 32 * (k + kQkAhead));
+      }
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        sc[mb][k & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[k % (kQkAhead + 1)][mb], qreg[k], sc[mb][k & 1], 0, 0, 0);
+    }
+    const f32x4 sacc[2] = {sc[0][0] + sc[0][1], sc[1][0] + sc[1][1]};
+
+    // a5: online softmax.  Lane holds tokens 16mb + 4g + r of head `head`.
+    const int tile_valid = n_valid - t * kTileTokens;
+    float x[2][4];
+    float tmax = -INFINITY;   // this tile's max per head
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = (16 * mb + 4 * g + r) < tile_valid;
+        x[mb][r] = ok ? sacc[mb][r] * p.scale_log2 : -INFINITY;
+        tmax = fmaxf(tmax, x[mb][r]);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    if (wid == 0 && t < 4) TS(8 + t);
+    // Lazy rescale: O and l keep a reference max m_run; they are rescaled only
+    // when some head of the wave sees its max rise by more than kRescaleLog2,
+    // so P = exp2(x - m_run) stays <= 2^kRescaleLog2 (exact in fp16 range).
+    // The quotient O / l is the same for any reference, so this changes no
+    // result beyond rounding.
+    if (__ballot(tmax > m_run + kRescaleLog2) != 0) {   // wave-uniform
+      const float m_new = fmaxf(m_run, tmax);          // finite: the tile has a valid token
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < 28; ++i) oacc[i] *= alpha;
+      m_run = m_new;
+    }
+    float rsum = 0.f;
+    f16x8 pb;   // P^T operand, k-slot 8g + 4mb + r
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float e = __builtin_amdgcn_exp2f(x[mb][r] - m_run);
+        rsum += e;
+        pb[4 * mb + r] = (_Float16)e;
+      }
+    rsum += __shfl_xor(rsum, 16);
+    rsum += __shfl_xor(rsum, 32);
+    l_run += rsum;
+
+    // a6: O^T[dim][head] += V^T P^T over the tile's 32 k-slots; the V^T
+    // operand comes from the token-major V tile through transposing reads:
+    // lane (g, c) addresses row 8g + c/4 (+4), dims d0 + 4(c%4), and receives
+    // V[8g..8g+3 (+4)][d0 + c].  Operands are read kPvAhead blocks ahead.
+    const uint16_t* vbase = &sm.v[buf][(8 * g + (col >> 2)) * kVRow + 4 * (col & 3)];
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    i16x4 vlo[kPvAhead + 1], vhi[kPvAhead + 1];
+#pragma unroll
+    for (int mb = 0; mb < kPvAhead; ++mb) {
+      vlo[mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 16 * mb));
+      vhi[mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 4 * kVRow + 16 * mb));
+    }
+#pragma unroll
+    for (int mb = 0; mb < 28; ++mb) {
+      const int nx = mb + kPvAhead;
+      if (nx < 28) {
+        vlo[nx % (kPvAhead + 1)] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 16 * nx));
+        vhi[nx % (kPvAhead + 1)] =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 4 * kVRow + 16 * nx));
+      }
+      const f16x4 lo = __builtin_bit_cast(f16x4, vlo[mb % (kPvAhead + 1)]);
+      const f16x4 hi = __builtin_bit_cast(f16x4, vhi[mb % (kPvAhead + 1)]);
+      const f16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      oacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb, oacc[mb], 0, 0, 0);
+    }
+    if (wid == 0 && t < 4) TS(12 + t);
+    __syncthreads();
+  }
+  if (wid == 0) TS(32);
+
+  // a7: epilogue.  Lane holds O^T[16mb + 4g + r][head].
+  const bool empty = !(l_run > 0.f);
+  const float inv = empty ? 0.f : 1.f / l_run;
+  const float lse_v = empty ? -INFINITY : (m_run + __builtin_amdgcn_logf(l_run)) * 0.69314718055994531f;
+  if (wid == 0) TS(35);
+  if (p.nsplit == 1) {
+    uint16_t* orow = p.out + ((int64_t)b * kHeads + head) * kDV + 4 * g;
+#pragma unroll
+    for (int mb = 0; mb < 28; ++mb) {
+      u32x2 w;
+      w.x = bf16x2_rne(oacc[mb][0] * inv, oacc[mb][1] * inv);
+      w.y = bf16x2_rne(oacc[mb][2] * inv, oacc[mb][3] * inv);
+      *(u32x2*)(orow + 16 * mb) = w;
+      if (wid == 0 && mb == 0) TS(36);
+    }
+    if (wid == 0) TS(37);
+    if (g == 0) p.lse[(int64_t)b * kHeads + head] = lse_v;
+  } else {
+    const int64_t pidx = ((int64_t)b * p.nsplit + s) * kHeads + head;
+    float* prow = p.part_o + pidx * kDV + 4 * g;
+#pragma unroll
+    for (int mb = 0; mb < 28; ++mb) *(f32x4*)(prow + 16 * mb) = oacc[mb] * inv;
+    if (g == 0) p.part_lse[pidx] = lse_v;
+  }
+  if (wid == 0) TS(33);
+  __builtin_amdgcn_s_waitcnt(0);
+  if (wid == 0) { TS(34); if (lane == 0 && blockIdx.x < 8192) g_tbuf[blockIdx.x * 40 + 39] = ntiles; }
+}
+
+// ---------------------------------------------------------------------------
+// a8: LSE combine of the slices of each query.
+// ---------------------------------------------------------------------------
+
+constexpr int kCombineHeads = 4;   // heads per combine workgroup
+
+__global__ __launch_bounds__(256) void mla_combine_kernel(const DecodeParams p) {
+  __shared__ float wts[kCombineHeads][32];
+  __shared__ float lse_out[kCombineHeads];
+  const int b = blockIdx.x / (kHeads / kCombineHeads);
+  const int h0 = (blockIdx.x % (kHeads / kCombineHeads)) * kCombineHeads;
+  const int ns = p.nsplit;
+  const int tid = threadIdx.x;
+  if (tid < kCombineHeads) {
+    const int h = h0 + tid;
+    float m = -INFINITY;
+    for (int s = 0; s < ns; ++s) m = fmaxf(m, p.part_lse[((int64_t)b * ns + s) * kHeads + h]);
+    float tot = 0.f;
+    for (int s = 0; s < ns; ++s) {
+      const float l = p.part_lse[((int64_t)b * ns + s) * kHeads + h];
+      const float w = (m == -INFINITY || l == -INFINITY) ? 0.f : __expf(l - m);
+      wts[tid][s] = w;
+      tot += w;
+    }
+    const float inv = tot > 0.f ? 1.f / tot : 0.f;
+    for (int s = 0; s < ns; ++s) wts[tid][s] *= inv;
+    lse_out[tid] = tot > 0.f ? m + __logf(tot) : -INFINITY;
+  }
+  __syncthreads();
+  constexpr int kVec = kDV / 4;   // float4 per head row
+  for (int e = tid; e < kCombineHeads * kVec; e += blockDim.x) {
+    const int hh = e / kVec, c4 = e - hh * kVec;
+    const int h = h0 + hh;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < ns; ++s) {
+      const float w = wts[hh][s];
+      if (w != 0.f) {
+        const f32x4 o = *(const f32x4*)(p.part_o + (((int64_t)b * ns + s) * kHeads + h) * kDV + 4 * c4);
+        acc += w * o;
+      }
+    }
+    u32x2 w2;
+    w2.x = bf16x2_rne(acc[0], acc[1]);
+    w2.y = bf16x2_rne(acc[2], acc[3]);
+    *(u32x2*)(p.out + ((int64_t)b * kHeads + h) * kDV + 4 * c4) = w2;
+  }
+  if (tid < kCombineHeads) p.lse[(int64_t)b * kHeads + h0 + tid] = lse_out[tid];
+}
+
+// ---------------------------------------------------------------------------
+// Test hook: a1-a3 exactly as the decode kernel runs them, then the LDS tiles
+// are written out per entry.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kThreads, 1) void mla_gather_kernel(const GatherParams p) {
+  __shared__ Smem sm;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int blk = logical_block(p.batch * p.nsplit);
+  const int b = blk / p.nsplit, s = blk - b * p.nsplit;
+  const int e0 = s * p.split_len;
+  const int n_ent = max(0, min(p.topk - e0, p.split_len));
+  const int32_t* idx_row = p.topk_idx + (int64_t)b * p.topk + e0;
+  const int32_t* pt_row = p.page_table + (int64_t)b * p.max_pages;
+  const int seq_len = p.seq_lens[b];
+
+  // masked entries: zero rows, valid = 0
+  for (int j = tid; j < n_ent; j += kThreads) {
+    int pg, sl;
+    const bool v = resolve_entry(idx_row[j], seq_len, pt_row, p.max_pages, p.num_pages, pg, sl);
+    const int64_t e = (int64_t)b * p.topk + e0 + j;
+    p.valid[e] = v ? 1 : 0;
+    if (!v) {
+      for (int d = 0; d < kDQK; d += 8) *(u32x4*)(p.k_rows + e * kDQK + d) = u32x4{0, 0, 0, 0};
+      for (int d = 0; d < kDV; d += 8) *(u32x4*)(p.v_rows + e * kDV + d) = u32x4{0, 0, 0, 0};
+    }
+  }
+
+  const int n_valid = compact_slice(sm, idx_row, n_ent, seq_len, pt_row, p.max_pages, p.num_pages);
+  const int ntiles = (n_valid + kTileTokens - 1) / kTileTokens;
+  TileRegs regs;
+  for (int t = 0; t < ntiles; ++t) {
+    if (wid >= kConsumers) {
+      const LastRecord last = {sm.tok[n_valid - 1][0], sm.tok[n_valid - 1][1]};
+      load_tile(regs, sm, p.kv, t, n_valid, last, wid - kConsumers, lane);
+      store_tile(sm, regs, 0, wid - kConsumers, lane);
+    }
+    __syncthreads();
+    for (int tt = wid; tt < kTileTokens; tt += kWaves) {
+      const int ci = t * kTileTokens + tt;
+      if (ci >= n_valid) continue;
+      const int64_t e = (int64_t)b * p.topk + e0 + sm.tok_entry[ci];
+      *(u32x4*)(p.k_rows + e * kDQK + 8 * lane) = *(const u32x4*)&sm.k[0][tt * kKRow + 8 * lane];
+      if (lane < 56)
+        *(u32x4*)(p.v_rows + e * kDV + 8 * lane) = *(const u32x4*)&sm.v[0][slot_of(tt) * kVRow + 8 * lane];
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
+  const int nblk = p.batch * p.nsplit;
+  hipLaunchKernelGGL(mla_decode_kernel, dim3(nblk), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const DecodeParams& p, hipStream_t stream) {
+  const int nblk = p.batch * (kHeads / kCombineHeads);
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(nblk), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const GatherParams& p, hipStream_t stream) {
+  const int nblk = p.batch * p.nsplit;
+  hipLaunchKernelGGL(mla_gather_kernel, dim3(nblk), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace mlasd
+
+extern "C" int mlasd_probe_read_timing(void* dst, size_t bytes) {
+  return (int)hipMemcpyFromSymbol(dst, HIP_SYMBOL(mlasd::g_tbuf), bytes, 0, hipMemcpyDeviceToHost);
+}
+extern "C" int mlasd_probe_skip_partials(int v) {
+  return (int)hipMemcpyToSymbol(HIP_SYMBOL(mlasd::g_skip_partials), &v, sizeof(int), 0, hipMemcpyHostToDevice);
+}

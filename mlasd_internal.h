@@ -1,0 +1,65 @@
+// Internal interface between the C-ABI layer and the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mlasd {
+
+// Shape of the method (64 heads share one latent KV head; 448 nope + 64 rope).
+constexpr int kHeads = 64;
+constexpr int kDNope = 448;
+constexpr int kDRope = 64;
+constexpr int kDQK = 512;
+constexpr int kDV = 448;
+constexpr int kMaxTopk = 512;
+// Paged cache layout: 256 token records of 576 B, then 256 scale records of 8 B.
+constexpr int kPageTokens = 256;
+constexpr int kRecordBytes = 576;
+constexpr int kScaleRecordBytes = 8;
+constexpr int64_t kPageBytes = 149504;
+constexpr int64_t kScaleBase = 147456;
+
+// Kernel tiling.
+constexpr int kTileTokens = 32;   // tokens per LDS tile
+constexpr int kThreads = 512;     // 8 waves: 4 head groups x 2 halves
+
+struct DecodeParams {
+  const uint16_t* q;          // bf16 [B, 64, 512]
+  const uint8_t* kv;          // [num_pages, 149504]
+  int64_t num_pages;
+  const int32_t* page_table;  // [B, max_pages]
+  int32_t max_pages;
+  const int32_t* topk_idx;    // [B, topk]
+  int32_t topk;
+  const int32_t* seq_lens;    // [B]
+  int32_t batch;
+  float scale_log2;           // softmax_scale * log2(e)
+  uint16_t* out;              // bf16 [B, 64, 448]
+  float* lse;                 // [B, 64]
+  float* part_o;              // [B, nsplit, 64, 448] when nsplit > 1
+  float* part_lse;            // [B, nsplit, 64]      when nsplit > 1
+  int32_t nsplit;
+  int32_t split_len;          // index entries per slice, multiple of kTileTokens
+};
+
+struct GatherParams {
+  const uint8_t* kv;
+  int64_t num_pages;
+  const int32_t* page_table;
+  int32_t max_pages;
+  const int32_t* topk_idx;
+  int32_t topk;
+  const int32_t* seq_lens;
+  int32_t batch;
+  uint16_t* k_rows;   // bf16 [B, topk, 512]
+  uint16_t* v_rows;   // fp16 [B, topk, 448]
+  uint8_t* valid;     // [B, topk]
+  int32_t nsplit;
+  int32_t split_len;
+};
+
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_combine(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_gather(const GatherParams& p, hipStream_t stream);
+
+}  // namespace mlasd

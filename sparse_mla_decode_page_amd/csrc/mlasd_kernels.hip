@@ -10,24 +10,24 @@
 // a whole number of 32-wide MFMA K-steps, so the pages' pad-to-512 mask has
 // nothing to do on this hardware.
 //
-// Workgroup = (query b, slice s of its top-k list), 512 threads = 8 waves.
-// Wave w: head group hg = w & 3 owns heads [16hg, 16hg+16); half dh = w >> 2
-// picks which 16 tokens of each 32-token tile it scores and which 224 of the
-// 448 output dims it accumulates.  The two waves of a head group swap their
-// softmax partials through LDS, so each holds P for all 32 tokens.
-//   a1  the slice's entries are validated, resolved through the page table
-//       and compacted (valid ones only) into an LDS list once;
-//   a2  each wave gathers 4 token records (576 B + 8 B scale record) straight
-//       into registers, three tiles ahead of the compute, with loads whose
-//       issue never depends on data (masked slots read page 0, slot 0);
-//   a3  dequantised with the gfx950 scaled fp8 conversions into an LDS K tile
-//       (bf16, token-major) and V tile (fp16, token-major, rows in PV k-slot
-//       order), both double-buffered;
-//   a4  S^T = K Q^T on v_mfma_f32_16x16x32_bf16, Q held in registers;
-//   a5  online softmax in fp32 (exp2 domain), one head per lane column;
-//   a6  O^T += V^T P^T on v_mfma_f32_16x16x32_f16, the V^T operand read with
-//       ds_read_b64_tr_b16 transposing loads, O^T in registers;
-//   a7  epilogue: bf16 out + fp32 lse, or fp32 partials for the combine;
+// Workgroup = (query b, slice s of its top-k list), 512 threads = 8 waves in
+// two roles, one wave of each role per SIMD, meeting at one barrier per
+// 32-token tile:
+//   consumers (waves 0..3): wave c owns heads [16c, 16c+16) and runs
+//       a4  S^T = K Q^T on v_mfma_f32_16x16x32_bf16, Q held in registers;
+//       a5  online softmax in fp32 (exp2 domain), one head per lane column;
+//       a6  O^T += V^T P^T on v_mfma_f32_16x16x32_f16 over all 448 dims, the
+//           V^T operand read with ds_read_b64_tr_b16 transposing loads;
+//       a7  epilogue: bf16 out + fp32 lse, or fp32 partials for the combine;
+//   producers (waves 4..7): wave p owns tokens [8p, 8p+8) of every tile and
+//       a2  gathers their records (576 B + 8 B scale record) into registers
+//           four tiles ahead, with loads whose issue never depends on data
+//           (masked slots re-read the slice's last valid record);
+//       a3  dequantises tile t+1 into the other LDS buffer (K bf16 token-major,
+//           V fp16 token-major with rows in PV k-slot order) while the
+//           consumers work on tile t.
+//   a1  before that, all waves validate, resolve through the page table and
+//       compact the slice's entries into an LDS list;
 //   a8  the combine kernel merges slices with the LSE rule.
 #include "mlasd_internal.h"
 
@@ -44,17 +44,19 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = kThreads / 64;
+constexpr int kConsumers = 4;       // waves 0..3
 constexpr int kKRow = kDQK + 8;     // K tile row stride (bf16 elements), +16 B pad
-constexpr int kVRow = kDV + 8;      // V tile row stride (fp16 elements), +16 B pad
-constexpr int kDepth = 3;           // tiles gathered ahead of the compute
-constexpr int kHalfDims = kDV / 2;  // output dims per wave: 224 = 14 MFMA rows of 16
+constexpr int kVRow = kDQK + 16;    // V tile row stride (fp16 elements): 448 dims, a
+                                    // 64-element spill area for lanes 56..63, +32 B pad
+constexpr int kDepth = 4;           // tiles gathered ahead by the producers
+constexpr int kTokPerProducer = kTileTokens / (kWaves - kConsumers);   // 8
+constexpr float kRescaleLog2 = 8.f; // lazy-rescale threshold (P <= 256)
+constexpr int kPvAhead = 3;         // PV operand blocks read ahead
+constexpr int kQkAhead = 2;         // QK^T operand k-steps read ahead
 
 struct __align__(16) Smem {
   uint16_t k[2][kTileTokens * kKRow];   // 2 x 33,280 B
-  uint16_t v[2][kTileTokens * kVRow];   // 2 x 29,184 B
-  f32x4 xp[2][kWaves][64];              // softmax partial exchange (p, 4 tokens/lane)
-  float xm[2][kWaves][16];              //                          (tile max per head)
-  u32x4 sink[2][8];                     // write target of the scale-record lanes 56..63
+  uint16_t v[2][kTileTokens * kVRow];   // 2 x 33,792 B
   int32_t tok[kMaxTopk][2];             // compacted list: physical page, slot
   uint16_t tok_entry[kMaxTopk];         //                 entry index in the slice
   int32_t wave_cnt[kWaves];
@@ -131,61 +133,74 @@ __device__ int compact_slice(Smem& sm, const int32_t* idx_row, int n_ent, int se
   return total;
 }
 
-// PV k-slot of tile token t.  Wave (hg, dh) scores tokens 16dh + 4g + r
-// (g = lane group, r = accumulator row), which feed k-slots 8g + 4dh + r of
-// the P^T operand; the V tile stores token t in row slot_of(t).
+// PV k-slot of tile token t.  A consumer's S^T accumulator block mb holds
+// tokens 16mb + 4g + r in lane group g, row r; they feed k-slots 8g + 4mb + r
+// of the P^T operand, so the V tile stores token t in row slot_of(t).
 __device__ __forceinline__ int slot_of(int t) { return 8 * ((t >> 2) & 3) + 4 * (t >> 4) + (t & 3); }
 
-// a2 registers of one tile for one wave: tokens 4w + j, j = 0..3.
+// a2 registers of one tile for one producer wave p: tokens 8p + j, j = 0..7.
 //   rec[j]: lanes 0..55 hold nope bytes [8 lane, 8 lane + 8) of token j,
 //           lanes 56..63 hold token j's 8-byte scale record;
-//   rope  : rope bytes [8 (lane & 15), +8) of token lane >> 4.
+//   rope  : rope bytes [16 (lane & 7), +16) of token lane >> 3.
+// Tile positions past the last valid entry re-read the slice's last valid
+// record (already cached); their scores are masked, so they add nothing.
 struct TileRegs {
-  u32x2 rec[4];
-  u32x2 rope;
+  u32x2 rec[kTokPerProducer];
+  u32x4 rope;
+};
+
+struct LastRecord {   // wave-uniform: the slice's last valid (page, slot)
+  int page, slot;
 };
 
 __device__ __forceinline__ void load_tile(TileRegs& r, const Smem& sm, const uint8_t* kv, int tile,
-                                          int n_valid, int wid, int lane) {
-  const int c0 = tile * kTileTokens + 4 * wid;
-  const int cc = min(c0, kMaxTopk - 4);
-  const i32x4 t01 = *(const i32x4*)&sm.tok[cc][0];      // tokens 0,1: page, slot, page, slot
-  const i32x4 t23 = *(const i32x4*)&sm.tok[cc + 2][0];  // tokens 2,3
-  const int pg[4] = {t01.x, t01.z, t23.x, t23.z};
-  const int sl[4] = {t01.y, t01.w, t23.y, t23.w};
+                                          int n_valid, LastRecord last, int pw, int lane) {
+  const int c0 = tile * kTileTokens + kTokPerProducer * pw;
+  const int cc = min(c0, kMaxTopk - kTokPerProducer);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const bool ok = c0 + j < n_valid;
-    const int64_t page = ok ? pg[j] : 0;
-    const int slot = ok ? sl[j] : 0;
-    const uint8_t* base = kv + page * kPageBytes;
-    const uint8_t* a = lane < 56 ? base + slot * kRecordBytes + 8 * lane
-                                 : base + kScaleBase + slot * kScaleRecordBytes;
-    r.rec[j] = *(const u32x2*)a;
+  for (int q = 0; q < kTokPerProducer / 2; ++q) {
+    const i32x4 t2 = *(const i32x4*)&sm.tok[cc + 2 * q][0];   // page, slot, page, slot
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int j = 2 * q + h;
+      const bool ok = c0 + j < n_valid;
+      // page and slot are the same in every lane: address math on the SALU
+      const int page = __builtin_amdgcn_readfirstlane(ok ? (h ? t2.z : t2.x) : last.page);
+      const int slot = __builtin_amdgcn_readfirstlane(ok ? (h ? t2.w : t2.y) : last.slot);
+      const uint8_t* base = kv + (int64_t)page * kPageBytes;
+      const uint32_t off = lane < 56 ? (uint32_t)(slot * kRecordBytes + 8 * lane)
+                                     : (uint32_t)(kScaleBase + slot * kScaleRecordBytes);
+      r.rec[j] = *(const u32x2*)(base + off);
+    }
   }
   {
-    const int j = lane >> 4;
-    const bool ok = c0 + j < n_valid;
-    const int64_t page = ok ? pg[j] : 0;
-    const int slot = ok ? sl[j] : 0;
-    r.rope = *(const u32x2*)(kv + page * kPageBytes + slot * kRecordBytes + kDNope + 8 * (lane & 15));
+    const int j = lane >> 3;
+    const int ci = c0 + j;
+    int page = last.page, slot = last.slot;
+    if (ci < n_valid) {
+      page = sm.tok[ci][0];
+      slot = sm.tok[ci][1];
+    }
+    r.rope = *(const u32x4*)(kv + (int64_t)page * kPageBytes + slot * kRecordBytes + kDNope + 16 * (lane & 7));
   }
 }
 
-// a3: dequantise one wave's 4 gathered tokens into LDS buffer `buf`.
-// Masked tile positions are written as zeros (zero K rows, zero V rows).
-__device__ __forceinline__ void store_tile(Smem& sm, const TileRegs& r, int buf, int tile, int n_valid,
-                                           int wid, int lane) {
-  const int c0 = tile * kTileTokens + 4 * wid;
+// a3: dequantise one producer wave's 8 gathered tokens into LDS buffer `buf`.
+// Every lane stores 16 bytes per row at 16 * lane: lanes 0..55 hold dims
+// [8 lane, 8 lane + 8); lanes 56..63 (the scale-record lanes) land in the K
+// row's rope span, rewritten just after by the rope store, and in the V row's
+// spill area, which PV never reads.
+__device__ __forceinline__ void store_tile(Smem& sm, const TileRegs& r, int buf, int pw, int lane) {
   const int g = lane >> 3;  // scale group of nope dims [8 lane, 8 lane + 8)
+  uint16_t* kb = &sm.k[buf][8 * lane];
+  uint16_t* vb = &sm.v[buf][8 * lane];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const bool ok = c0 + j < n_valid;
+  for (int j = 0; j < kTokPerProducer; ++j) {
     const uint32_t lo = __builtin_amdgcn_readlane(r.rec[j].x, 56);
     const uint32_t hi = __builtin_amdgcn_readlane(r.rec[j].y, 56);
     const uint32_t sb = ((g < 4) ? (lo >> (8 * g)) : (hi >> (8 * (g - 4)))) & 0xffu;
     const float scale = __uint_as_float(sb << 23);   // 2^(sb-127) as an fp32 power of two
-    const uint32_t b0 = ok ? r.rec[j].x : 0u, b1 = ok ? r.rec[j].y : 0u;
+    const uint32_t b0 = r.rec[j].x, b1 = r.rec[j].y;
     u32x4 kq, vq;
     kq.x = pack2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b0, scale, false));
     kq.y = pack2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b0, scale, true));
@@ -195,40 +210,85 @@ __device__ __forceinline__ void store_tile(Smem& sm, const TileRegs& r, int buf,
     vq.y = pack2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b0, scale, true));
     vq.z = pack2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b1, scale, false));
     vq.w = pack2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b1, scale, true));
-    const int t = 4 * wid + j;
-    // lanes 56..63 carry the scale record, not nope bytes: their stores go to
-    // a sink instead of a branch (keeps the load-wait counting exact).
-    u32x4* kd = lane < 56 ? (u32x4*)&sm.k[buf][t * kKRow + 8 * lane] : &sm.sink[0][lane & 7];
-    u32x4* vd = lane < 56 ? (u32x4*)&sm.v[buf][slot_of(t) * kVRow + 8 * lane] : &sm.sink[1][lane & 7];
-    *kd = kq;
-    *vd = vq;
+    const int t = kTokPerProducer * pw + j;
+    *(u32x4*)(kb + t * kKRow) = kq;
+    *(u32x4*)(vb + slot_of(t) * kVRow) = vq;
   }
-  const int jr = lane >> 4;
-  const bool ok = c0 + jr < n_valid;
-  *(u32x2*)&sm.k[buf][(4 * wid + jr) * kKRow + kDNope + 4 * (lane & 15)] =
-      ok ? r.rope : u32x2{0u, 0u};
+  const int tr = kTokPerProducer * pw + (lane >> 3);
+  *(u32x4*)&sm.k[buf][tr * kKRow + kDNope + 8 * (lane & 7)] = r.rope;
 }
 
 // ---------------------------------------------------------------------------
 // a1-a7: main decode kernel
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeParams p) {
+// A kernel argument read late in a long kernel is re-fetched from the
+// argument segment (a fresh memory round trip); pin what the epilogue needs
+// into scalar registers at entry instead.
+template <typename T>
+__device__ __forceinline__ T* pin_ptr(T* ptr) {
+  const uint64_t v = (uint64_t)ptr;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (T*)(((uint64_t)hi << 32) | lo);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeParams p_arg) {
   __shared__ Smem sm;
+  DecodeParams p = p_arg;
+  p.out = pin_ptr(p_arg.out);
+  p.lse = pin_ptr(p_arg.lse);
+  p.part_o = pin_ptr(p_arg.part_o);
+  p.part_lse = pin_ptr(p_arg.part_lse);
+  p.nsplit = __builtin_amdgcn_readfirstlane(p_arg.nsplit);
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int hg = wid & 3, dh = wid >> 2, partner = wid ^ 4;
-  const int g = lane >> 4;         // MFMA lane group
-  const int col = lane & 15;       // MFMA column: head within the head group
   const int blk = logical_block(p.batch * p.nsplit);
   const int b = blk / p.nsplit, s = blk - b * p.nsplit;
   const int e0 = s * p.split_len;
   const int n_ent = max(0, min(p.topk - e0, p.split_len));
-  const int head = 16 * hg + col;
 
   const int n_valid = compact_slice(sm, p.topk_idx + (int64_t)b * p.topk + e0, n_ent,
                                     p.seq_lens[b], p.page_table + (int64_t)b * p.max_pages,
                                     p.max_pages, p.num_pages);
   const int ntiles = (n_valid + kTileTokens - 1) / kTileTokens;
+
+  // Both roles pass the same barriers: one after the first tile is stored,
+  // then one per tile.
+  if (wid >= kConsumers) {
+    // ---------------- producers: a2 + a3 ----------------
+    const int pw = wid - kConsumers;
+    if (ntiles == 0) {   // empty slice: nothing to gather
+      __syncthreads();
+      return;
+    }
+    const LastRecord last = {__builtin_amdgcn_readfirstlane(sm.tok[n_valid - 1][0]),
+                             __builtin_amdgcn_readfirstlane(sm.tok[n_valid - 1][1])};
+    TileRegs regs[kDepth];
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) load_tile(regs[u], sm, p.kv, u, n_valid, last, pw, lane);
+    store_tile(sm, regs[0], 0, pw, lane);
+    load_tile(regs[0], sm, p.kv, kDepth, n_valid, last, pw, lane);
+    __syncthreads();
+    for (int t0 = 0; t0 < ntiles; t0 += kDepth) {
+#pragma unroll
+      for (int u = 0; u < kDepth; ++u) {
+        const int t = t0 + u;
+        const int nxt = (u + 1) % kDepth;   // ring slot of tile t + 1
+        if (t + 1 < ntiles) store_tile(sm, regs[nxt], (t + 1) & 1, pw, lane);
+        // issued on every path, so the loads in flight behind each ring slot
+        // are the same wherever it is consumed (past the end they re-read a
+        // cached record)
+        load_tile(regs[nxt], sm, p.kv, t + 1 + kDepth, n_valid, last, pw, lane);
+        if (t < ntiles) __syncthreads();
+      }
+    }
+    return;
+  }
+
+  // ---------------- consumers: a4 - a7 ----------------
+  const int g = lane >> 4;         // MFMA lane group
+  const int col = lane & 15;       // MFMA column: head within the wave's 16
+  const int head = 16 * wid + col;
 
   // Q^T operand for the wave's 16 heads, kept in registers: dims [32k + 8g, +8).
   bf16x8 qreg[16];
@@ -237,124 +297,125 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
 #pragma unroll
     for (int k = 0; k < 16; ++k) qreg[k] = *(const bf16x8*)(qrow + 32 * k);
   }
-
-  TileRegs regs[kDepth];
+  f32x4 oacc[28];
 #pragma unroll
-  for (int u = 0; u < kDepth; ++u) load_tile(regs[u], sm, p.kv, u, n_valid, wid, lane);
-
-  f32x4 oacc[14];
-#pragma unroll
-  for (int i = 0; i < 14; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < 28; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
+  __syncthreads();
 
-  for (int t0 = 0; t0 < ntiles; t0 += kDepth) {
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    // a4: S^T[token][head] for the tile's 32 tokens: two 16-token blocks,
+    // two accumulation chains each, operands read kQkAhead k-steps ahead.
+    const uint16_t* krow = &sm.k[buf][col * kKRow + 8 * g];
+    bf16x8 ka[kQkAhead + 1][2];
 #pragma unroll
-    for (int u = 0; u < kDepth; ++u) {
-      const int t = t0 + u;
-      const int buf = t & 1;
-      if (t < ntiles) store_tile(sm, regs[u], buf, t, n_valid, wid, lane);
-      // the gather for tile t + kDepth is issued on every path, so the number
-      // of loads in flight behind regs[u] is the same wherever it is consumed
-      load_tile(regs[u], sm, p.kv, t + kDepth, n_valid, wid, lane);
-      if (t < ntiles) {
-        __syncthreads();
-
-        // a4: S^T[token][head] for this wave's 16 tokens; two accumulation chains.
-        const uint16_t* krow = &sm.k[buf][(16 * dh + col) * kKRow + 8 * g];
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < kQkAhead; ++k)
 #pragma unroll
-        for (int k = 0; k < 16; k += 2) {
-          const bf16x8 a0 = *(const bf16x8*)(krow + 32 * k);
-          const bf16x8 a1 = *(const bf16x8*)(krow + 32 * (k + 1));
-          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qreg[k], s0, 0, 0, 0);
-          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qreg[k + 1], s1, 0, 0, 0);
-        }
-        const f32x4 sacc = s0 + s1;
-
-        // a5: own tokens 16dh + 4g + r; tile max and exp against it.
-        const int tile_valid = n_valid - t * kTileTokens;
-        float x[4], m_own = -INFINITY;
+      for (int mb = 0; mb < 2; ++mb) ka[k][mb] = *(const bf16x8*)(krow + 16 * mb * kKRow + 32 * k);
+    f32x4 sc[2][2] = {};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool ok = (16 * dh + 4 * g + r) < tile_valid;
-          x[r] = ok ? sacc[r] * p.scale_log2 : -INFINITY;
-          m_own = fmaxf(m_own, x[r]);
-        }
-        m_own = fmaxf(m_own, __shfl_xor(m_own, 16));
-        m_own = fmaxf(m_own, __shfl_xor(m_own, 32));
-        f32x4 p_own;
+    for (int k = 0; k < 16; ++k) {
+      if (k + kQkAhead < 16) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          p_own[r] = (m_own == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x[r] - m_own);
-        sm.xp[buf][wid][lane] = p_own;
-        if (g == 0) sm.xm[buf][wid][col] = m_own;
-        __syncthreads();
-        const f32x4 p_part = sm.xp[buf][partner][lane];
-        const float m_part = sm.xm[buf][partner][col];
-
-        const float m_new = fmaxf(m_run, fmaxf(m_own, m_part));   // finite
-        const float c_own = (m_own == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_own - m_new);
-        const float c_part = (m_part == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_part - m_new);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        // P^T operand in k-slot order 8g + 4*half + r (half 0 = tokens 0..15).
-        float pk[8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float po = p_own[r] * c_own, pp = p_part[r] * c_part;
-          pk[r] = dh == 0 ? po : pp;
-          pk[4 + r] = dh == 0 ? pp : po;
-        }
-        float rsum = 0.f;
-        f16x8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          rsum += pk[e];
-          pb[e] = (_Float16)pk[e];
-        }
-        rsum += __shfl_xor(rsum, 16);
-        rsum += __shfl_xor(rsum, 32);
-        l_run = l_run * alpha + rsum;
-        m_run = m_new;
-
-        // a6: O^T[dim][head] = alpha O^T + V^T P^T over the tile's 32 k-slots;
-        // the V^T operand comes from the token-major V tile through
-        // transposing reads: lane (g, c) addresses row 8g + c/4 (+4), dims
-        // d0 + 4(c%4), and receives V[8g..8g+3 (+4)][d0 + c].
-        const uint16_t* vbase = &sm.v[buf][(8 * g + (col >> 2)) * kVRow + kHalfDims * dh + 4 * (col & 3)];
-#pragma unroll
-        for (int mb = 0; mb < 14; ++mb) {
-          typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-          const f16x4 lo = __builtin_bit_cast(
-              f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 16 * mb)));
-          const f16x4 hi = __builtin_bit_cast(
-              f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 4 * kVRow + 16 * mb)));
-          const f16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          oacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb, oacc[mb] * alpha, 0, 0, 0);
-        }
+        for (int mb = 0; mb < 2; ++mb)
+          ka[(k + kQkAhead) % (kQkAhead + 1)][mb] = *(const bf16x8*)(krow + 16 * mb * kKRow + 32 * (k + kQkAhead));
       }
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        sc[mb][k & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[k % (kQkAhead + 1)][mb], qreg[k], sc[mb][k & 1], 0, 0, 0);
     }
+    const f32x4 sacc[2] = {sc[0][0] + sc[0][1], sc[1][0] + sc[1][1]};
+
+    // a5: online softmax.  Lane holds tokens 16mb + 4g + r of head `head`.
+    const int tile_valid = n_valid - t * kTileTokens;
+    float x[2][4];
+    float tmax = -INFINITY;   // this tile's max per head
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = (16 * mb + 4 * g + r) < tile_valid;
+        x[mb][r] = ok ? sacc[mb][r] * p.scale_log2 : -INFINITY;
+        tmax = fmaxf(tmax, x[mb][r]);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    // Lazy rescale: O and l keep a reference max m_run; they are rescaled only
+    // when some head of the wave sees its max rise by more than kRescaleLog2,
+    // so P = exp2(x - m_run) stays <= 2^kRescaleLog2 (exact in fp16 range).
+    // The quotient O / l is the same for any reference, so this changes no
+    // result beyond rounding.
+    if (__ballot(tmax > m_run + kRescaleLog2) != 0) {   // wave-uniform
+      const float m_new = fmaxf(m_run, tmax);          // finite: the tile has a valid token
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < 28; ++i) oacc[i] *= alpha;
+      m_run = m_new;
+    }
+    float rsum = 0.f;
+    f16x8 pb;   // P^T operand, k-slot 8g + 4mb + r
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float e = __builtin_amdgcn_exp2f(x[mb][r] - m_run);
+        rsum += e;
+        pb[4 * mb + r] = (_Float16)e;
+      }
+    rsum += __shfl_xor(rsum, 16);
+    rsum += __shfl_xor(rsum, 32);
+    l_run += rsum;
+
+    // a6: O^T[dim][head] += V^T P^T over the tile's 32 k-slots; the V^T
+    // operand comes from the token-major V tile through transposing reads:
+    // lane (g, c) addresses row 8g + c/4 (+4), dims d0 + 4(c%4), and receives
+    // V[8g..8g+3 (+4)][d0 + c].  Operands are read kPvAhead blocks ahead.
+    const uint16_t* vbase = &sm.v[buf][(8 * g + (col >> 2)) * kVRow + 4 * (col & 3)];
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    i16x4 vlo[kPvAhead + 1], vhi[kPvAhead + 1];
+#pragma unroll
+    for (int mb = 0; mb < kPvAhead; ++mb) {
+      vlo[mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 16 * mb));
+      vhi[mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 4 * kVRow + 16 * mb));
+    }
+#pragma unroll
+    for (int mb = 0; mb < 28; ++mb) {
+      const int nx = mb + kPvAhead;
+      if (nx < 28) {
+        vlo[nx % (kPvAhead + 1)] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 16 * nx));
+        vhi[nx % (kPvAhead + 1)] =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 4 * kVRow + 16 * nx));
+      }
+      const f16x4 lo = __builtin_bit_cast(f16x4, vlo[mb % (kPvAhead + 1)]);
+      const f16x4 hi = __builtin_bit_cast(f16x4, vhi[mb % (kPvAhead + 1)]);
+      const f16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      oacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb, oacc[mb], 0, 0, 0);
+    }
+    __syncthreads();
   }
 
-  // a7: epilogue.  Lane holds O^T[224dh + 16mb + 4g + r][head].
+  // a7: epilogue.  Lane holds O^T[16mb + 4g + r][head].
   const bool empty = !(l_run > 0.f);
   const float inv = empty ? 0.f : 1.f / l_run;
   const float lse_v = empty ? -INFINITY : (m_run + __builtin_amdgcn_logf(l_run)) * 0.69314718055994531f;
   if (p.nsplit == 1) {
-    uint16_t* orow = p.out + ((int64_t)b * kHeads + head) * kDV + kHalfDims * dh + 4 * g;
+    uint16_t* orow = p.out + ((int64_t)b * kHeads + head) * kDV + 4 * g;
 #pragma unroll
-    for (int mb = 0; mb < 14; ++mb) {
+    for (int mb = 0; mb < 28; ++mb) {
       u32x2 w;
       w.x = bf16x2_rne(oacc[mb][0] * inv, oacc[mb][1] * inv);
       w.y = bf16x2_rne(oacc[mb][2] * inv, oacc[mb][3] * inv);
       *(u32x2*)(orow + 16 * mb) = w;
     }
-    if (dh == 0 && g == 0) p.lse[(int64_t)b * kHeads + head] = lse_v;
+    if (g == 0) p.lse[(int64_t)b * kHeads + head] = lse_v;
   } else {
     const int64_t pidx = ((int64_t)b * p.nsplit + s) * kHeads + head;
-    float* prow = p.part_o + pidx * kDV + kHalfDims * dh + 4 * g;
+    float* prow = p.part_o + pidx * kDV + 4 * g;
 #pragma unroll
-    for (int mb = 0; mb < 14; ++mb) *(f32x4*)(prow + 16 * mb) = oacc[mb] * inv;
-    if (dh == 0 && g == 0) p.part_lse[pidx] = lse_v;
+    for (int mb = 0; mb < 28; ++mb) *(f32x4*)(prow + 16 * mb) = oacc[mb] * inv;
+    if (g == 0) p.part_lse[pidx] = lse_v;
   }
 }
 
@@ -439,8 +500,11 @@ __global__ __launch_bounds__(kThreads, 1) void mla_gather_kernel(const GatherPar
   const int ntiles = (n_valid + kTileTokens - 1) / kTileTokens;
   TileRegs regs;
   for (int t = 0; t < ntiles; ++t) {
-    load_tile(regs, sm, p.kv, t, n_valid, wid, lane);
-    store_tile(sm, regs, 0, t, n_valid, wid, lane);
+    if (wid >= kConsumers) {
+      const LastRecord last = {sm.tok[n_valid - 1][0], sm.tok[n_valid - 1][1]};
+      load_tile(regs, sm, p.kv, t, n_valid, last, wid - kConsumers, lane);
+      store_tile(sm, regs, 0, wid - kConsumers, lane);
+    }
     __syncthreads();
     for (int tt = wid; tt < kTileTokens; tt += kWaves) {
       const int ci = t * kTileTokens + tt;
@@ -477,3 +541,4 @@ hipError_t launch_gather(const GatherParams& p, hipStream_t stream) {
 }
 
 }  // namespace mlasd
+
