@@ -90,6 +90,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="per-launch HBM bytes measured with rocprofv3 counters")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager calls only (for counter-collection runs)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run 8 plain device-to-device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -104,9 +108,18 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    mlasd.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(8):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "copies": 8}), flush=True)
+        return
+    mlasd.load_library()
 
     t0 = time.perf_counter()
     w = make_config(args.config)
@@ -156,6 +169,12 @@ def main():
         ev1.record(side)
     side.synchronize()
     eager_ms = ev0.elapsed_time(ev1) / n_eager
+
+    if args.no_graph:
+        res = {"metric": "eager only", "ms_per_step": eager_ms, "steps": n_eager,
+               "config": {"workload": CONFIG_NAMES[args.config], "nsplit": nsplit}}
+        print(json.dumps(res), flush=True)
+        return
 
     # one graph = one pass over all input sets; replayed until >= steps
     graph = torch.cuda.CUDAGraph()

@@ -41,8 +41,9 @@
  *     into slices) is owned by the library: one buffer per (device, stream),
  *     grown with hipMalloc when a call needs more and kept until the process
  *     ends.  Calls on different streams may run concurrently; calls on one
- *     stream are ordered by the stream.  Growth synchronises the stream, so
- *     under graph capture make a first call of the largest shape beforehand.
+ *     stream are ordered by the stream.  Growth synchronises the stream and
+ *     is refused with MLASD_ERR_CAPTURE while the stream is capturing a
+ *     graph: make a first call of the largest shape before capture.
  */
 #ifndef MLASD_H
 #define MLASD_H
@@ -63,7 +64,8 @@ enum {
   MLASD_ERR_ALIGN = -3,     /* a pointer is not aligned as stated                 */
   MLASD_ERR_VALUE = -4,     /* a scalar argument is invalid (non-finite scale)    */
   MLASD_ERR_HIP = -5,       /* a HIP runtime call failed (see mlasd_last_hip_error) */
-  MLASD_ERR_DEVICE = -6     /* the current device is not a gfx950 device          */
+  MLASD_ERR_DEVICE = -6,    /* the current device is not a gfx950 device          */
+  MLASD_ERR_CAPTURE = -7    /* split scratch would have to grow during graph capture */
 };
 
 /* Fixed shape of the method. */

@@ -42,10 +42,11 @@ int device_cus(int* cus) {
   return MLASD_OK;
 }
 
-// Split scratch: one buffer per (device, stream), grown on demand and kept
-// for the life of the process.  Growing synchronises that stream before the
-// old buffer is freed, so it must not happen during graph capture: a first
-// call with the largest shape outside capture sizes it.
+// Split scratch: one buffer per (device, stream) for the fp32 partials of
+// the slices, grown on demand and kept for the life of the process.
+// Growing synchronises the stream and frees the old buffer, so it is refused
+// while the stream is capturing: a first call with the largest shape outside
+// capture sizes it.
 struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
@@ -60,6 +61,10 @@ int stream_workspace(hipStream_t stream, size_t bytes, void** out) {
   std::lock_guard<std::mutex> lock(g_ws_mu);
   Workspace& w = g_ws[{dev, stream}];
   if (w.bytes < bytes) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(stream, &cs);
+    if (e != hipSuccess) return hip_fail(e);
+    if (cs != hipStreamCaptureStatusNone) return MLASD_ERR_CAPTURE;
     if (w.ptr) {
       e = hipStreamSynchronize(stream);
       if (e != hipSuccess) return hip_fail(e);
@@ -78,8 +83,12 @@ int stream_workspace(hipStream_t stream, size_t bytes, void** out) {
 }
 
 // Split plan: one workgroup per (query, top-k slice).  Without a request the
-// slices are sized so the grid covers every compute unit once; a slice holds
-// a whole number of 32-token tiles.
+// slices are sized so the grid covers every compute unit once, but no slice
+// is cut below kMinAutoSlice entries: a workgroup needs a few tiles for its
+// gather to overlap its contractions, and every extra slice costs a partial
+// write and read.  A slice holds a whole number of 32-token tiles.
+constexpr int kMinAutoSlice = 128;
+
 void make_plan(int32_t batch, int32_t topk, int32_t request, int cus, int32_t* nsplit,
                int32_t* split_len) {
   const int tile = mlasd::kTileTokens;
@@ -89,6 +98,8 @@ void make_plan(int32_t batch, int32_t topk, int32_t request, int cus, int32_t* n
     ns = request;
   } else {
     ns = batch > 0 ? (cus + batch - 1) / batch : 1;
+    const int by_len = topk > 0 ? (topk + kMinAutoSlice - 1) / kMinAutoSlice : 1;
+    if (ns > by_len) ns = by_len;
   }
   if (ns > max_split) ns = max_split;
   if (ns < 1) ns = 1;
@@ -228,6 +239,7 @@ const char* mlasd_status_string(int status) {
     case MLASD_ERR_VALUE: return "invalid scalar argument";
     case MLASD_ERR_HIP: return "HIP runtime error";
     case MLASD_ERR_DEVICE: return "current device is not gfx950";
+    case MLASD_ERR_CAPTURE: return "split scratch would have to grow while the stream is capturing";
     default: return "unknown status";
   }
 }

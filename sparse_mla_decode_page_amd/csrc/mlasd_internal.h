@@ -21,7 +21,7 @@ constexpr int64_t kScaleBase = 147456;
 
 // Kernel tiling.
 constexpr int kTileTokens = 32;   // tokens per LDS tile
-constexpr int kThreads = 512;     // 8 waves: 4 head groups x 2 halves
+constexpr int kThreads = 512;     // 8 waves: 4 consumers + 4 producers
 
 struct DecodeParams {
   const uint16_t* q;          // bf16 [B, 64, 512]

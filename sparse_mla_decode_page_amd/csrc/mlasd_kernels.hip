@@ -41,6 +41,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = kThreads / 64;
@@ -53,6 +54,8 @@ constexpr int kTokPerProducer = kTileTokens / (kWaves - kConsumers);   // 8
 constexpr float kRescaleLog2 = 8.f; // lazy-rescale threshold (P <= 256)
 constexpr int kPvAhead = 3;         // PV operand blocks read ahead
 constexpr int kQkAhead = 2;         // QK^T operand k-steps read ahead
+constexpr int kStageRowBytes = 912; // epilogue staging row: 896 B (+16 B pad)
+constexpr int kStageBytes = 16 * kStageRowBytes;   // one wave's 16 rows
 
 struct __align__(16) Smem {
   uint16_t k[2][kTileTokens * kKRow];   // 2 x 33,280 B
@@ -61,6 +64,8 @@ struct __align__(16) Smem {
   uint16_t tok_entry[kMaxTopk];         //                 entry index in the slice
   int32_t wave_cnt[kWaves];
 };
+static_assert(2 * kStageBytes <= (int)sizeof(Smem::k[0]) && 2 * kStageBytes <= (int)sizeof(Smem::v[0]),
+              "epilogue staging must fit one K and one V buffer");
 
 // ---------------------------------------------------------------------------
 // small helpers
@@ -153,36 +158,38 @@ struct LastRecord {   // wave-uniform: the slice's last valid (page, slot)
   int page, slot;
 };
 
+// Per-lane record offset within a page is slot * mul + add: lanes 0..55 read
+// nope bytes [8 lane, +8) of the 576-byte record, lanes 56..63 the 8-byte
+// scale record in the page's scale area.
+struct LaneOffset {
+  uint32_t mul, add;
+};
+
+__device__ __forceinline__ LaneOffset lane_offset(int lane) {
+  return lane < 56 ? LaneOffset{(uint32_t)kRecordBytes, 8u * lane}
+                   : LaneOffset{(uint32_t)kScaleRecordBytes, (uint32_t)kScaleBase};
+}
+
 __device__ __forceinline__ void load_tile(TileRegs& r, const Smem& sm, const uint8_t* kv, int tile,
-                                          int n_valid, LastRecord last, int pw, int lane) {
+                                          int n_valid, LastRecord last, int pw, int lane,
+                                          LaneOffset lo) {
   const int c0 = tile * kTileTokens + kTokPerProducer * pw;
-  const int cc = min(c0, kMaxTopk - kTokPerProducer);
+  // Lane l resolves token c0 + l/8 with one LDS read; token j's page and slot
+  // are then broadcast from lane 8j, so the address math is scalar and no
+  // load waits on another.
+  const int ci = c0 + (lane >> 3);
+  const i32x2 ps = *(const i32x2*)&sm.tok[min(ci, kMaxTopk - 1)][0];
+  const bool ok = ci < n_valid;
+  const int page = ok ? ps.x : last.page;
+  const int slot = ok ? ps.y : last.slot;
 #pragma unroll
-  for (int q = 0; q < kTokPerProducer / 2; ++q) {
-    const i32x4 t2 = *(const i32x4*)&sm.tok[cc + 2 * q][0];   // page, slot, page, slot
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int j = 2 * q + h;
-      const bool ok = c0 + j < n_valid;
-      // page and slot are the same in every lane: address math on the SALU
-      const int page = __builtin_amdgcn_readfirstlane(ok ? (h ? t2.z : t2.x) : last.page);
-      const int slot = __builtin_amdgcn_readfirstlane(ok ? (h ? t2.w : t2.y) : last.slot);
-      const uint8_t* base = kv + (int64_t)page * kPageBytes;
-      const uint32_t off = lane < 56 ? (uint32_t)(slot * kRecordBytes + 8 * lane)
-                                     : (uint32_t)(kScaleBase + slot * kScaleRecordBytes);
-      r.rec[j] = *(const u32x2*)(base + off);
-    }
+  for (int j = 0; j < kTokPerProducer; ++j) {
+    const int pg = __builtin_amdgcn_readlane(page, 8 * j);
+    const int sl = __builtin_amdgcn_readlane(slot, 8 * j);
+    const uint8_t* base = kv + (int64_t)pg * kPageBytes;
+    r.rec[j] = *(const u32x2*)(base + (__umul24((uint32_t)sl, lo.mul) + lo.add));
   }
-  {
-    const int j = lane >> 3;
-    const int ci = c0 + j;
-    int page = last.page, slot = last.slot;
-    if (ci < n_valid) {
-      page = sm.tok[ci][0];
-      slot = sm.tok[ci][1];
-    }
-    r.rope = *(const u32x4*)(kv + (int64_t)page * kPageBytes + slot * kRecordBytes + kDNope + 16 * (lane & 7));
-  }
+  r.rope = *(const u32x4*)(kv + (int64_t)page * kPageBytes + slot * kRecordBytes + kDNope + 16 * (lane & 7));
 }
 
 // a3: dequantise one producer wave's 8 gathered tokens into LDS buffer `buf`.
@@ -222,25 +229,8 @@ __device__ __forceinline__ void store_tile(Smem& sm, const TileRegs& r, int buf,
 // a1-a7: main decode kernel
 // ---------------------------------------------------------------------------
 
-// A kernel argument read late in a long kernel is re-fetched from the
-// argument segment (a fresh memory round trip); pin what the epilogue needs
-// into scalar registers at entry instead.
-template <typename T>
-__device__ __forceinline__ T* pin_ptr(T* ptr) {
-  const uint64_t v = (uint64_t)ptr;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (T*)(((uint64_t)hi << 32) | lo);
-}
-
-__global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeParams p_arg) {
+__global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeParams p) {
   __shared__ Smem sm;
-  DecodeParams p = p_arg;
-  p.out = pin_ptr(p_arg.out);
-  p.lse = pin_ptr(p_arg.lse);
-  p.part_o = pin_ptr(p_arg.part_o);
-  p.part_lse = pin_ptr(p_arg.part_lse);
-  p.nsplit = __builtin_amdgcn_readfirstlane(p_arg.nsplit);
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int blk = logical_block(p.batch * p.nsplit);
   const int b = blk / p.nsplit, s = blk - b * p.nsplit;
@@ -259,27 +249,28 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
     const int pw = wid - kConsumers;
     if (ntiles == 0) {   // empty slice: nothing to gather
       __syncthreads();
-      return;
-    }
-    const LastRecord last = {__builtin_amdgcn_readfirstlane(sm.tok[n_valid - 1][0]),
-                             __builtin_amdgcn_readfirstlane(sm.tok[n_valid - 1][1])};
-    TileRegs regs[kDepth];
+    } else {
+      const LastRecord last = {__builtin_amdgcn_readfirstlane(sm.tok[n_valid - 1][0]),
+                               __builtin_amdgcn_readfirstlane(sm.tok[n_valid - 1][1])};
+      const LaneOffset lo = lane_offset(lane);
+      TileRegs regs[kDepth];
 #pragma unroll
-    for (int u = 0; u < kDepth; ++u) load_tile(regs[u], sm, p.kv, u, n_valid, last, pw, lane);
-    store_tile(sm, regs[0], 0, pw, lane);
-    load_tile(regs[0], sm, p.kv, kDepth, n_valid, last, pw, lane);
-    __syncthreads();
-    for (int t0 = 0; t0 < ntiles; t0 += kDepth) {
+      for (int u = 0; u < kDepth; ++u) load_tile(regs[u], sm, p.kv, u, n_valid, last, pw, lane, lo);
+      store_tile(sm, regs[0], 0, pw, lane);
+      load_tile(regs[0], sm, p.kv, kDepth, n_valid, last, pw, lane, lo);
+      __syncthreads();
+      for (int t0 = 0; t0 < ntiles; t0 += kDepth) {
 #pragma unroll
-      for (int u = 0; u < kDepth; ++u) {
-        const int t = t0 + u;
-        const int nxt = (u + 1) % kDepth;   // ring slot of tile t + 1
-        if (t + 1 < ntiles) store_tile(sm, regs[nxt], (t + 1) & 1, pw, lane);
-        // issued on every path, so the loads in flight behind each ring slot
-        // are the same wherever it is consumed (past the end they re-read a
-        // cached record)
-        load_tile(regs[nxt], sm, p.kv, t + 1 + kDepth, n_valid, last, pw, lane);
-        if (t < ntiles) __syncthreads();
+        for (int u = 0; u < kDepth; ++u) {
+          const int t = t0 + u;
+          const int nxt = (u + 1) % kDepth;   // ring slot of tile t + 1
+          if (t + 1 < ntiles) store_tile(sm, regs[nxt], (t + 1) & 1, pw, lane);
+          // issued on every path, so the loads in flight behind each ring slot
+          // are the same wherever it is consumed (past the end they re-read a
+          // cached record)
+          load_tile(regs[nxt], sm, p.kv, t + 1 + kDepth, n_valid, last, pw, lane, lo);
+          if (t < ntiles) __syncthreads();
+        }
       }
     }
     return;
@@ -400,22 +391,44 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
   const bool empty = !(l_run > 0.f);
   const float inv = empty ? 0.f : 1.f / l_run;
   const float lse_v = empty ? -INFINITY : (m_run + __builtin_amdgcn_logf(l_run)) * 0.69314718055994531f;
+  // The wave's 16 output rows are contiguous in memory.  They are staged
+  // through LDS so each store writes 1 KB of whole cache lines instead of 16
+  // scattered 32-byte pieces: the store rate is bound by write requests in
+  // flight per CU, and this cuts them four-fold.  The staging area is the LDS
+  // buffer the last tile did not use; every wave finished its reads of it
+  // before the last barrier, and the producers write no LDS after it.
+  const int eb = ntiles & 1;
+  uint8_t* stage = (uint8_t*)(wid < 2 ? &sm.k[eb][0] : &sm.v[eb][0]) + (wid & 1) * kStageBytes;
   if (p.nsplit == 1) {
-    uint16_t* orow = p.out + ((int64_t)b * kHeads + head) * kDV + 4 * g;
 #pragma unroll
     for (int mb = 0; mb < 28; ++mb) {
       u32x2 w;
       w.x = bf16x2_rne(oacc[mb][0] * inv, oacc[mb][1] * inv);
       w.y = bf16x2_rne(oacc[mb][2] * inv, oacc[mb][3] * inv);
-      *(u32x2*)(orow + 16 * mb) = w;
+      *(u32x2*)(stage + col * kStageRowBytes + 2 * (16 * mb + 4 * g)) = w;
+    }
+    uint8_t* obase = (uint8_t*)(p.out + ((int64_t)b * kHeads + 16 * wid) * kDV);
+#pragma unroll
+    for (int k = 0; k < 14; ++k) {   // 16 rows x 896 B = 14 x 1 KB
+      const int i = lane + 64 * k, row = i / 56, ch = i - 56 * row;
+      *(u32x4*)(obase + 16 * i) = *(const u32x4*)(stage + row * kStageRowBytes + 16 * ch);
     }
     if (g == 0) p.lse[(int64_t)b * kHeads + head] = lse_v;
   } else {
-    const int64_t pidx = ((int64_t)b * p.nsplit + s) * kHeads + head;
-    float* prow = p.part_o + pidx * kDV + 4 * g;
+    const int64_t prow0 = ((int64_t)b * p.nsplit + s) * kHeads + 16 * wid;
 #pragma unroll
-    for (int mb = 0; mb < 28; ++mb) *(f32x4*)(prow + 16 * mb) = oacc[mb] * inv;
-    if (g == 0) p.part_lse[pidx] = lse_v;
+    for (int h = 0; h < 2; ++h) {   // fp32 partials, 224 dims per pass
+#pragma unroll
+      for (int mb = 0; mb < 14; ++mb)
+        *(f32x4*)(stage + col * kStageRowBytes + 4 * (16 * mb + 4 * g)) = oacc[14 * h + mb] * inv;
+#pragma unroll
+      for (int k = 0; k < 14; ++k) {   // 16 rows x 224 floats = 14 x 1 KB
+        const int i = lane + 64 * k, row = i / 56, ch = i - 56 * row;
+        *(f32x4*)(p.part_o + (prow0 + row) * kDV + kDV / 2 * h + 4 * ch) =
+            *(const f32x4*)(stage + row * kStageRowBytes + 16 * ch);
+      }
+    }
+    if (g == 0) p.part_lse[((int64_t)b * p.nsplit + s) * kHeads + head] = lse_v;
   }
 }
 
@@ -502,7 +515,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_gather_kernel(const GatherPar
   for (int t = 0; t < ntiles; ++t) {
     if (wid >= kConsumers) {
       const LastRecord last = {sm.tok[n_valid - 1][0], sm.tok[n_valid - 1][1]};
-      load_tile(regs, sm, p.kv, t, n_valid, last, wid - kConsumers, lane);
+      load_tile(regs, sm, p.kv, t, n_valid, last, wid - kConsumers, lane, lane_offset(lane));
       store_tile(sm, regs, 0, wid - kConsumers, lane);
     }
     __syncthreads();

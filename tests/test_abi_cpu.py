@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = m.load_library()
-    for code in (0, -1, -2, -3, -4, -5, -6):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert m.status_string(code) != "unknown status"
     assert m.status_string(-99) == "unknown status"
     assert lib.mlasd_version().decode().startswith("mlasd")
@@ -87,16 +87,19 @@ def test_gather_hook_validation_without_device():
 
 @pytest.mark.parametrize("batch,topk,req,cus,expect", [
     (64, 512, 0, 256, (4, 128)),     # one workgroup per compute unit
-    (1, 512, 0, 256, (16, 32)),      # small batch: every 32-token tile its own slice
-    (16, 512, 0, 256, (16, 32)),
+    (1, 512, 0, 256, (4, 128)),      # small batch: slices of at least 128 entries
+    (16, 512, 0, 256, (4, 128)),
+    (128, 512, 0, 256, (2, 256)),
     (256, 512, 0, 256, (1, 512)),    # batch fills the GPU: no split
-    (1, 64, 0, 256, (2, 32)),
-    (3, 45, 0, 256, (2, 32)),        # ragged top-k
+    (1, 64, 0, 256, (1, 64)),
+    (3, 300, 0, 256, (3, 128)),      # ragged top-k
+    (3, 45, 0, 256, (1, 64)),
     (1, 0, 0, 256, (1, 32)),         # empty top-k: one slice, writes zeros / -inf
     (64, 512, 1, 256, (1, 512)),     # forced
     (64, 512, 3, 256, (3, 192)),     # slices hold whole 32-token tiles
     (64, 512, 99, 256, (16, 32)),    # clamped to ceil(topk/32)
-    (8, 100, 0, 80, (4, 32)),
+    (8, 100, 0, 80, (1, 128)),
+    (32, 512, 0, 80, (3, 192)),
 ])
 def test_plan(batch, topk, req, cus, expect):
     ns, sl = m.plan(batch, topk, req, cus)

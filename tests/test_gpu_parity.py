@@ -2,6 +2,7 @@
 
 Gather + dequant must match bit for bit; attention outputs within
 |d| <= 2e-3 + 1e-2 |ref| (out) and |d| <= 1e-3 (lse)."""
+import dataclasses
 import math
 
 import numpy as np
@@ -283,3 +284,38 @@ def test_graph_capture_replay():
         mlasd.mla_sparse_decode(d["q"], d["kv_pages"], d["page_table"], d["topk_idx"], d["seq_lens"],
                                 w.softmax_scale)
         torch.cuda.synchronize()
+
+
+def test_split_merge_alternating_inputs():
+    """The fused LSE merge reads partials written by other workgroups of the
+    same launch: alternate two input sets of one shape on one stream, with no
+    host synchronisation between launches, and check every result against
+    the first result of its set (bitwise) and against the oracle.  A merge
+    that read a stale partial of the previous launch would differ."""
+    base = config(3)[0]
+    # rotation_sets writes records into the pool: work on a copy
+    w, w2 = G.rotation_sets(dataclasses.replace(base, kv_pages=base.kv_pages.copy()), 2, seed=4242)
+    ref_out, ref_lse = O.sparse_mla_decode(w.q_bits, w.kv_pages, w.page_table, w.topk_idx,
+                                           w.seq_lens, w.softmax_scale)
+    ref2 = O.sparse_mla_decode(w2.q_bits, w2.kv_pages, w2.page_table, w2.topk_idx, w2.seq_lens,
+                               w2.softmax_scale)
+    d1, d2 = to_device(w), to_device(w2)
+    for ns in (4, 16):
+        res = []
+        for it in range(8):
+            d = d1 if it % 2 == 0 else d2
+            o, l = mlasd.mla_sparse_decode(d["q"], d["kv_pages"], d["page_table"], d["topk_idx"],
+                                           d["seq_lens"], w.softmax_scale, nsplit=ns)
+            res.append((o, l))
+        torch.cuda.synchronize()
+        for it, (o, l) in enumerate(res):
+            o0, l0 = res[it % 2]
+            assert torch.equal(o, o0) and torch.equal(l, l0), f"nsplit={ns} launch {it}"
+        check_attention(res[0][0], res[0][1], ref_out, ref_lse, label=f"set A nsplit={ns}")
+        check_attention(res[1][0], res[1][1], ref2[0], ref2[1], label=f"set B nsplit={ns}")
+    # the arrival counters are back at zero: a smaller batch on the same stream
+    ws = G.make_config(2)
+    ref_s = O.sparse_mla_decode(ws.q_bits, ws.kv_pages, ws.page_table, ws.topk_idx, ws.seq_lens,
+                                ws.softmax_scale)
+    o, l = run(ws, nsplit=4)
+    check_attention(o, l, ref_s[0], ref_s[1], label="smaller batch after")
