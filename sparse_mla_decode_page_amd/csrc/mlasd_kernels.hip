@@ -49,7 +49,7 @@ constexpr int kConsumers = 4;       // waves 0..3
 constexpr int kKRow = kDQK + 8;     // K tile row stride (bf16 elements), +16 B pad
 constexpr int kVRow = kDQK + 16;    // V tile row stride (fp16 elements): 448 dims, a
                                     // 64-element spill area for lanes 56..63, +32 B pad
-constexpr int kDepth = 4;           // tiles gathered ahead by the producers
+constexpr int kDepth = 2;           // tiles gathered ahead by the producers
 constexpr int kTokPerProducer = kTileTokens / (kWaves - kConsumers);   // 8
 constexpr float kRescaleLog2 = 8.f; // lazy-rescale threshold (P <= 256)
 constexpr int kPvAhead = 3;         // PV operand blocks read ahead
@@ -436,49 +436,49 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
 // a8: LSE combine of the slices of each query.
 // ---------------------------------------------------------------------------
 
-constexpr int kCombineHeads = 4;   // heads per combine workgroup
+constexpr int kCombineThreads = 128;   // one workgroup per (query, head); 112 float4 per row
 
-__global__ __launch_bounds__(256) void mla_combine_kernel(const DecodeParams p) {
-  __shared__ float wts[kCombineHeads][32];
-  __shared__ float lse_out[kCombineHeads];
-  const int b = blockIdx.x / (kHeads / kCombineHeads);
-  const int h0 = (blockIdx.x % (kHeads / kCombineHeads)) * kCombineHeads;
-  const int ns = p.nsplit;
-  const int tid = threadIdx.x;
-  if (tid < kCombineHeads) {
-    const int h = h0 + tid;
-    float m = -INFINITY;
-    for (int s = 0; s < ns; ++s) m = fmaxf(m, p.part_lse[((int64_t)b * ns + s) * kHeads + h]);
-    float tot = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const float l = p.part_lse[((int64_t)b * ns + s) * kHeads + h];
-      const float w = (m == -INFINITY || l == -INFINITY) ? 0.f : __expf(l - m);
-      wts[tid][s] = w;
-      tot += w;
+// Every thread loads all it needs at once -- the slices' lse values of its
+// head and its float4 of every slice's partial row -- so the merge costs one
+// memory round trip.  Weights: w_s = exp(lse_s - max) / sum; empty slices
+// (lse = -inf) get 0; a query with no valid entry gets out = 0, lse = -inf.
+__global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(const DecodeParams p) {
+  const int b = blockIdx.x / kHeads, h = blockIdx.x - b * kHeads;
+  const int ns = p.nsplit;   // <= kMaxTopk / kTileTokens = 16
+  const int c4 = threadIdx.x;
+  const float* pl = p.part_lse + (int64_t)b * ns * kHeads + h;
+  const float* po = p.part_o + ((int64_t)b * ns * kHeads + h) * kDV + 4 * c4;
+  float l[16];
+  f32x4 o[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    if (k < ns) {
+      l[k] = pl[k * kHeads];
+      if (c4 < kDV / 4) o[k] = *(const f32x4*)(po + (int64_t)k * kHeads * kDV);
     }
-    const float inv = tot > 0.f ? 1.f / tot : 0.f;
-    for (int s = 0; s < ns; ++s) wts[tid][s] *= inv;
-    lse_out[tid] = tot > 0.f ? m + __logf(tot) : -INFINITY;
   }
-  __syncthreads();
-  constexpr int kVec = kDV / 4;   // float4 per head row
-  for (int e = tid; e < kCombineHeads * kVec; e += blockDim.x) {
-    const int hh = e / kVec, c4 = e - hh * kVec;
-    const int h = h0 + hh;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < ns; ++s) {
-      const float w = wts[hh][s];
-      if (w != 0.f) {
-        const f32x4 o = *(const f32x4*)(p.part_o + (((int64_t)b * ns + s) * kHeads + h) * kDV + 4 * c4);
-        acc += w * o;
-      }
+  float m = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < 16; ++k)
+    if (k < ns) m = fmaxf(m, l[k]);
+  float tot = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    if (k < ns) {
+      const float w = (m == -INFINITY) ? 0.f : __expf(l[k] - m);   // exp(-inf) = 0 for empty slices
+      tot += w;
+      acc += w * o[k];
     }
+  }
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  if (c4 < kDV / 4) {
     u32x2 w2;
-    w2.x = bf16x2_rne(acc[0], acc[1]);
-    w2.y = bf16x2_rne(acc[2], acc[3]);
+    w2.x = bf16x2_rne(acc[0] * inv, acc[1] * inv);
+    w2.y = bf16x2_rne(acc[2] * inv, acc[3] * inv);
     *(u32x2*)(p.out + ((int64_t)b * kHeads + h) * kDV + 4 * c4) = w2;
   }
-  if (tid < kCombineHeads) p.lse[(int64_t)b * kHeads + h0 + tid] = lse_out[tid];
+  if (c4 == 0) p.lse[(int64_t)b * kHeads + h] = tot > 0.f ? m + __logf(tot) : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -542,8 +542,8 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_combine(const DecodeParams& p, hipStream_t stream) {
-  const int nblk = p.batch * (kHeads / kCombineHeads);
-  hipLaunchKernelGGL(mla_combine_kernel, dim3(nblk), dim3(256), 0, stream, p);
+  const int nblk = p.batch * kHeads;
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(nblk), dim3(kCombineThreads), 0, stream, p);
   return hipGetLastError();
 }
 
