@@ -46,6 +46,14 @@ Readings where the pages are silent (each is listed in the design notes):
       Every valid entry counts once, duplicates included.
   R5  lse is the natural log of the sum of exp over the *scaled* scores.
   R6  A query with no valid entry gets out = 0 and lse = -inf.
+  R7  (cache append) A token latent is quantised per 64-dim group: the scale
+      exponent k is the least integer with amax <= 448 * 2^k, clamped to
+      [-127, 127] (amax = 0 gives -127); the scale byte is k + 127; every value
+      is encoded as the e4m3 code nearest to x * 2^-k, ties to the even code,
+      sign kept (also for zero).  Scale byte 7 is written as 0.  The rope
+      values are stored as they are.  A token is written at position p of
+      sequence s when 0 <= s < B, p >= 0, p // 256 < max_pages and the
+      physical page lies in the pool; otherwise it is skipped.
 """
 from __future__ import annotations
 
@@ -208,3 +216,75 @@ def lse_combine(outs, lses):
     wn = np.where(finite, w / np.where(finite, total, 1.0), 0.0)
     out = (wn[..., None] * np.where(np.isfinite(lses)[..., None], outs, 0.0)).sum(axis=0)
     return out, lse
+
+
+# ----------------------------------------------------------------------------
+# cache append: quantise token latents into records (reading R7)
+# ----------------------------------------------------------------------------
+
+def scale_exponent(amax):
+    """Least integer k with amax <= 448 * 2^k, clamped to [-127, 127]; amax = 0
+    gives -127.  A floating log only proposes a start; the answer is settled
+    by exact comparisons with the powers of two."""
+    amax = float(amax)
+    if amax == 0.0:
+        return -127
+    k = int(np.floor(np.log2(amax / 448.0))) - 2
+    while 448.0 * 2.0 ** k < amax:
+        k += 1
+    return max(-127, min(127, k))
+
+
+_FINITE_CODES = np.array([c for c in range(128) if not np.isnan(_E4M3_TABLE[c])], dtype=np.int64)
+
+
+def e4m3_encode_nearest(y):
+    """e4m3 code of the value nearest to y (|y| <= 448), ties to the even code,
+    sign bit copied from y (so -0.0 gives 0x80).  Plain search over the table
+    of all finite non-negative codes."""
+    y = float(y)
+    a = abs(y)
+    vals = _E4M3_TABLE[_FINITE_CODES]
+    d = np.abs(vals - a)
+    best = d.min()
+    cands = _FINITE_CODES[d == best]
+    code = int(cands[0]) if len(cands) == 1 else int(cands[cands % 2 == 0][0])
+    return code | (0x80 if np.signbit(y) else 0)
+
+
+def quantize_token(latent_bits):
+    """One token latent (bf16 bits [512]: 448 nope, 64 rope) -> (the 576-byte
+    token record, the 8-byte scale record) (reading R7)."""
+    bits = np.asarray(latent_bits, dtype=np.uint16)
+    x = bf16_value(bits[:NOPE])
+    rec = np.zeros(RECORD_BYTES, dtype=np.uint8)
+    sc = np.zeros(SCALE_RECORD_BYTES, dtype=np.uint8)
+    for g in range(NOPE // SCALE_GROUP):
+        xs = x[g * SCALE_GROUP:(g + 1) * SCALE_GROUP]
+        k = scale_exponent(np.abs(xs).max())
+        sc[g] = k + 127
+        for d in range(SCALE_GROUP):
+            rec[g * SCALE_GROUP + d] = e4m3_encode_nearest(xs[d] * 2.0 ** -k)
+    rec[NOPE:] = bits[NOPE:].astype("<u2").view(np.uint8)
+    return rec, sc
+
+
+def kv_append(kv_pages, page_table, seq_ids, positions, latent_bits):
+    """A copy of the pool with every valid token written (reading R7)."""
+    kv = np.array(kv_pages, dtype=np.uint8, copy=True)
+    pt = np.asarray(page_table, dtype=np.int64)
+    B, max_pages = pt.shape
+    num_pages = kv.shape[0]
+    for i in range(len(positions)):
+        s, p = int(seq_ids[i]), int(positions[i])
+        if not (0 <= s < B and p >= 0 and p // TOKENS_PER_PAGE < max_pages):
+            continue
+        page = int(pt[s, p // TOKENS_PER_PAGE])
+        if not 0 <= page < num_pages:
+            continue
+        slot = p % TOKENS_PER_PAGE
+        rec, sc = quantize_token(latent_bits[i])
+        kv[page, slot * RECORD_BYTES:(slot + 1) * RECORD_BYTES] = rec
+        kv[page, SCALE_REGION + slot * SCALE_RECORD_BYTES:SCALE_REGION + (slot + 1) * SCALE_RECORD_BYTES] = sc
+    return kv
+

@@ -319,3 +319,21 @@ def test_split_merge_alternating_inputs():
                                 ws.softmax_scale)
     o, l = run(ws, nsplit=4)
     check_attention(o, l, ref_s[0], ref_s[1], label="smaller batch after")
+
+
+# ----------------------------------------------------------------------------
+# the pages' validation matrix ("The Moment of Validation", "The Third
+# Attempt"): B in {1, 4, 16, 32}, 64 heads, topk in {128, 512}
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("batch", [1, 4, 16, 32])
+@pytest.mark.parametrize("topk", [128, 512])
+def test_validation_matrix(batch, topk):
+    lens = [4096 + 97 * b for b in range(batch)]
+    w = G.build_workload(31000 + 10 * batch + topk, lens, topk, name=f"B={batch} topk={topk}")
+    ref_out, ref_lse = O.sparse_mla_decode(w.q_bits, w.kv_pages, w.page_table, w.topk_idx,
+                                           w.seq_lens, w.softmax_scale)
+    for ns in (None, 1):
+        out, lse = run(w, nsplit=ns)
+        check_attention(out, lse, ref_out, ref_lse,
+                        label=f"B={batch:2d} H=64 topk={topk} nsplit={ns or 'plan'}")

@@ -323,3 +323,112 @@ def test_decimal_brute_force_tiny():
         for c in (0, 100, 447):
             v = sum(x.exp() / z * Decimal(float(rows[t, c])) for t, x in enumerate(s))
             assert abs(float(v) - out[0, h, c]) < 1e-13 * max(1.0, abs(float(v)))
+
+
+# ----------------------------------------------------------------------------
+# cache append: the quantiser (reading R7)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("amax,k", [(448.0, 0), (449.0, 1), (224.0, -1), (224.5, 0), (1.0, -8),
+                                    (0.0, -127), (2.0 ** 200, 127), (2.0 ** -200, -127),
+                                    (448.0 * 2.0 ** -20, -20), (448.0 * 2.0 ** -20 * (1 + 2 ** -30), -19)])
+def test_append_scale_exponent_closed_form(amax, k):
+    assert O.scale_exponent(amax) == k
+
+
+def test_append_scale_exponent_brackets_amax():
+    rng = np.random.default_rng(5)
+    for amax in np.exp(rng.uniform(-60, 60, 2000)):
+        k = O.scale_exponent(amax)
+        assert 448.0 * 2.0 ** (k - 1) < amax <= 448.0 * 2.0 ** k
+
+
+def test_append_encode_roundtrips_every_code():
+    for code in range(256):
+        v = O.e4m3_value(code)
+        if np.isnan(v):
+            continue
+        y = -0.0 if code == 0x80 else float(v)
+        assert O.e4m3_encode_nearest(y) == code, hex(code)
+
+
+def test_append_encode_ties_to_even():
+    finite = sorted({float(O.e4m3_value(c)) for c in range(127) if not np.isnan(O.e4m3_value(c))})
+    for lo, hi in zip(finite, finite[1:]):
+        mid = (lo + hi) / 2.0
+        code = O.e4m3_encode_nearest(mid)
+        assert code % 2 == 0 and float(O.e4m3_value(code)) in (lo, hi)
+
+
+def test_append_encode_matches_torch_rne_cast():
+    rng = np.random.default_rng(6)
+    y = np.concatenate([rng.uniform(-448, 448, 3000), rng.uniform(-1, 1, 3000) * 2.0 ** -5,
+                        rng.standard_normal(3000)])
+    mine = np.array([O.e4m3_encode_nearest(v) for v in y], dtype=np.uint8)
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(mine, ref)
+
+
+def _latents(n, seed):
+    """bf16 latents: N(0,1) groups, one 20-sigma group, an all-zero group, a
+    tiny-magnitude group and a group with exact e4m3 values."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, 512))
+    x[:, 64:128] *= 20.0
+    x[:, 128:192] = 0.0
+    x[:, 192:256] *= 2.0 ** -30
+    x[:, 256:320] = O.e4m3_value(rng.integers(0, 126, (n, 64))) * 2.0 ** 3
+    return G.bf16_bits(x)
+
+
+def test_append_quantize_token_error_bound_and_layout():
+    bits = _latents(40, 7)
+    for row in bits:
+        rec, sc = O.quantize_token(row)
+        x = O.bf16_value(row[:448]).reshape(7, 64)
+        assert sc[7] == 0
+        assert np.array_equal(rec[448:].view("<u2"), row[448:])
+        dec = O.e4m3_value(rec[:448]).reshape(7, 64) * O.ue8m0_value(sc[:7])[:, None]
+        for g in range(7):
+            k = int(sc[g]) - 127
+            amax = np.abs(x[g]).max()
+            # half an e4m3 step: 2^-4 relative in the normal range, 2^-10 * 2^k below it
+            bound = np.maximum(np.abs(x[g]) * 2.0 ** -4, 2.0 ** (-10 + k))
+            assert np.all(np.abs(dec[g] - x[g]) <= bound)
+            if amax > 0:   # the scale is tight: the largest value lands in (224, 448]
+                assert 224.0 < amax * 2.0 ** -k <= 448.0
+        # exactly representable values come back exactly
+        assert np.array_equal(dec[4], x[4])
+
+
+def test_append_quantize_agrees_with_the_generator_quantiser():
+    """A second, independent implementation (frexp exponent, rint rounding)."""
+    bits = _latents(60, 8)
+    for row in bits:
+        rec, sc = O.quantize_token(row)
+        codes, scale = G.quantize_nope(O.bf16_value(row[:448])[None])
+        assert np.array_equal(rec[:448], codes[0]) and np.array_equal(sc[:7], scale[0])
+
+
+def test_append_writes_valid_tokens_only_and_decodes_back():
+    pool = np.full((4, O.BYTES_PER_PAGE), 0x5A, dtype=np.uint8)
+    pt = np.array([[2, 0], [1, -1]], dtype=np.int32)
+    seq = np.array([0, 0, 1, 1, 1, 2, -1, 0], dtype=np.int32)
+    pos = np.array([3, 300, 7, 256, -1, 0, 0, 600], dtype=np.int32)
+    bits = _latents(len(pos), 9)
+    out = O.kv_append(pool, pt, seq, pos, bits)
+    # written: (0,3) -> page 2 slot 3, (0,300) -> page 0 slot 44, (1,7) -> page 1 slot 7
+    written = {(2, 3): 0, (0, 44): 1, (1, 7): 2}
+    for (page, slot), i in written.items():
+        rows, ok = O.gather_dequant(out, np.array([[page]], dtype=np.int32),
+                                    np.array([[slot]], dtype=np.int32), np.array([256], dtype=np.int32))
+        rec, sc = O.quantize_token(bits[i])
+        want = np.concatenate([O.e4m3_value(rec[:448]) * np.repeat(O.ue8m0_value(sc[:7]), 64),
+                               O.bf16_value(bits[i][448:])])
+        assert ok.all() and np.array_equal(rows[0, 0], want)
+    # nothing else changed: (1,256) has no page, -1 / seq 2 / seq -1 / position 600 are invalid
+    mask = np.ones_like(out, dtype=bool)
+    for (page, slot) in written:
+        mask[page, slot * 576:(slot + 1) * 576] = False
+        mask[page, 147456 + slot * 8:147456 + slot * 8 + 8] = False
+    assert np.all(out[mask] == 0x5A)
