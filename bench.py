@@ -32,6 +32,7 @@ FLOP_PER_TOKEN = 2 * 64 * 512 + 2 * 64 * 448   # QK^T + PV per valid (query, tok
 Q_BYTES = 64 * 512 * 2
 OUT_BYTES = 64 * 448 * 2 + 64 * 4
 TOKEN_BYTES = 584
+APPEND_BYTES_PER_TOKEN = 512 * 2 + 4 + 4 + TOKEN_BYTES   # latent + seq id + position + record
 
 
 def log(*a):
@@ -78,6 +79,39 @@ def cpu_baseline(w, seconds):
                       f"numpy float64 with {threads} BLAS thread(s)"}
 
 
+def bench_append(dev, kv, pt, seq_len, steps, stream):
+    """Time mla_kv_append writing the last `per_seq` positions of every
+    sequence (a prefill-sized append of 4,096 tokens per sequence) into the
+    resident pool; HIP events on the launch stream around `steps` calls."""
+    import torch
+    import sparse_mla_decode_page_amd as mlasd
+    B = pt.shape[0]
+    per_seq = 4096
+    n = B * per_seq
+    g = torch.Generator(device="cpu").manual_seed(99)
+    lat = (torch.randn((n, 512), generator=g) * 2.0).to(torch.bfloat16).to(dev)
+    seq = torch.arange(B, dtype=torch.int32).repeat_interleave(per_seq).to(dev)
+    pos = (torch.arange(per_seq, dtype=torch.int32) + (seq_len - per_seq)).repeat(B).to(dev)
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            mlasd.mla_kv_append(lat, seq, pos, pt, kv, stream=stream)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            mlasd.mla_kv_append(lat, seq, pos, pt, kv, stream=stream)
+        e1.record(stream)
+    stream.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    byts = n * APPEND_BYTES_PER_TOKEN
+    gbs = byts / (us * 1e-6) / 1e9
+    return {"tokens_per_launch": n, "us_per_launch": us, "tokens_per_s": n / (us * 1e-6),
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                         "algorithmic_bytes_per_launch": byts},
+            "workload": f"{B} sequences x {per_seq} new tokens into the resident pool"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -92,6 +126,9 @@ def main():
                     help="per-launch HBM bytes measured with rocprofv3 counters")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager calls only (for counter-collection runs)")
+    ap.add_argument("--op", choices=["decode", "append"], default="decode",
+                    help="append: time only the cache-append kernel")
+    ap.add_argument("--no-append", action="store_true", help="skip the cache-append measurement")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 8 plain device-to-device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -131,6 +168,15 @@ def main():
     kv = torch.from_numpy(w.kv_pages).to(dev)
     pt = torch.from_numpy(w.page_table).to(dev)
     lens = torch.from_numpy(w.seq_lens).to(dev)
+    side = torch.cuda.Stream(dev)
+    if args.op == "append":
+        if int(w.seq_lens.min()) < 4096:
+            print("--op append needs every sequence >= 4096 tokens (config 1-3)", file=sys.stderr)
+            sys.exit(2)
+        res = bench_append(dev, kv, pt, int(w.seq_lens.min()), args.steps, side)
+        res["metric"] = "cache append: tokens/s"
+        print(json.dumps(res), flush=True)
+        return
     dsets = []
     for s in sets:
         dsets.append(dict(
@@ -141,7 +187,6 @@ def main():
     stats = [workload_stats(s) for s in sets]
     nsplit, split_len = mlasd.plan(w.batch, w.topk, args.nsplit)
     nsplit_arg = args.nsplit if args.nsplit > 0 else None
-    side = torch.cuda.Stream(dev)
 
     def step(i, stream):
         d = dsets[i % n_sets]
@@ -252,6 +297,9 @@ def main():
             "timed": "decode kernel" + (" + LSE combine kernel" if nsplit > 1 else ""),
         },
     }
+    if not args.no_append and int(w.seq_lens.min()) >= 4096:
+        # runs after the decode timing: it overwrites the pool's tail records
+        res["kv_append"] = bench_append(dev, kv, pt, int(w.seq_lens.min()), 50, side)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

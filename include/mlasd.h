@@ -155,6 +155,32 @@ int mla_sparse_gather_dequant(const void* kv_pages, int64_t num_pages,
                               void* k_rows, void* v_rows, uint8_t* valid,
                               mlasd_stream_t stream);
 
+/*
+ * mla_kv_append -- the step before the decode: quantise token latents into
+ * the paged cache ("The Turning Point", "Input Knowledge Required",
+ * FP8/UE8M0 bullet; layout as above, "The Validation Gate", "The Test
+ * Design").
+ *
+ *   latent     bf16 [n_tokens, 512]; 16-byte aligned.  Dims 0..447 nope,
+ *              448..511 rope.
+ *   seq_ids    int32 [n_tokens]: page-table row of each token.
+ *   positions  int32 [n_tokens]: position of each token in its sequence.
+ *   page_table int32 [batch, max_pages]; logical page -> physical page.
+ *   kv_pages   uint8 [num_pages, 149504]; 16-byte aligned; written.
+ *
+ * Token i goes to page page_table[s][p / 256], slot p % 256 (s = seq_ids[i],
+ * p = positions[i]).  Nope dims of group g (64 each) get scale byte
+ * k + 127, k the least integer with max|x| <= 448 * 2^k clamped to
+ * [-127, 127] (0 -> -127), and codes e4m3(round-to-nearest-even(x * 2^-k));
+ * scale byte 7 is 0; rope values are stored as they are.  Tokens whose
+ * sequence, position or page is out of range are skipped (not an error).
+ * Two tokens with the same destination in one call: either may win.
+ * n_tokens == 0 is a no-op.  Returns MLASD_OK or a negative MLASD_ERR_* code.
+ */
+int mla_kv_append(const void* latent, const int32_t* seq_ids, const int32_t* positions,
+                  int32_t n_tokens, const int32_t* page_table, int32_t batch, int32_t max_pages,
+                  void* kv_pages, int64_t num_pages, mlasd_stream_t stream);
+
 /* Static text for a status code. */
 const char* mlasd_status_string(int status);
 

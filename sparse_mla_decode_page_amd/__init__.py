@@ -7,11 +7,12 @@ from ._binding import (  # noqa: F401
     MlasdError,
     library_path,
     load_library,
+    mla_kv_append,
     mla_sparse_decode,
     mla_sparse_gather_dequant,
     plan,
     status_string,
 )
 
-__all__ = ["mla_sparse_decode", "mla_sparse_gather_dequant", "plan", "load_library",
+__all__ = ["mla_sparse_decode", "mla_sparse_gather_dequant", "mla_kv_append", "plan", "load_library",
            "library_path", "status_string", "MlasdError"]

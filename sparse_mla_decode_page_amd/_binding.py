@@ -51,6 +51,8 @@ def load_library():
     lib.mla_sparse_plan.restype = ctypes.c_int
     lib.mla_sparse_gather_dequant.argtypes = [vp, i64, vp, i32, vp, i32, vp, i32, vp, vp, vp, vp]
     lib.mla_sparse_gather_dequant.restype = ctypes.c_int
+    lib.mla_kv_append.argtypes = [vp, vp, vp, i32, vp, i32, i32, vp, i64, vp]
+    lib.mla_kv_append.restype = ctypes.c_int
     lib.mlasd_status_string.argtypes = [ctypes.c_int]
     lib.mlasd_status_string.restype = ctypes.c_char_p
     lib.mlasd_last_hip_error.argtypes = []
@@ -174,3 +176,32 @@ def mla_sparse_gather_dequant(kv_pages, page_table, topk_idx, seq_lens, stream=N
                                            _stream(stream, dev))
     _check(rc, "mla_sparse_gather_dequant")
     return k_rows, v_rows, valid
+
+
+def mla_kv_append(latent, seq_ids, positions, page_table, kv_pages, stream=None):
+    """Quantise token latents (bf16 [N, 512]) into the paged cache in place.
+    seq_ids / positions int32 [N]; page_table int32 [B, max_pages]."""
+    _need(latent, "latent", torch.bfloat16, 2)
+    _need(seq_ids, "seq_ids", torch.int32, 1)
+    _need(positions, "positions", torch.int32, 1)
+    _need(page_table, "page_table", torch.int32, 2)
+    _need(kv_pages, "kv_pages", torch.uint8, 2)
+    n = latent.shape[0]
+    if latent.shape[1] != D_QK:
+        raise ValueError(f"latent must be [N, {D_QK}]")
+    if seq_ids.shape[0] != n or positions.shape[0] != n:
+        raise ValueError("seq_ids / positions must have one entry per token")
+    if kv_pages.shape[1] != PAGE_BYTES:
+        raise ValueError(f"kv_pages rows must be {PAGE_BYTES} bytes")
+    dev = kv_pages.device
+    for t in (latent, seq_ids, positions, page_table):
+        if t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+    lib = load_library()
+    with torch.cuda.device(dev):
+        rc = lib.mla_kv_append(_ptr(latent), _ptr(seq_ids), _ptr(positions), n, _ptr(page_table),
+                               page_table.shape[0], page_table.shape[1], _ptr(kv_pages),
+                               kv_pages.shape[0], _stream(stream, dev))
+    _check(rc, "mla_kv_append")
+    return kv_pages
+

@@ -230,6 +230,34 @@ int mla_sparse_gather_dequant(const void* kv_pages, int64_t num_pages, const int
   return MLASD_OK;
 }
 
+int mla_kv_append(const void* latent, const int32_t* seq_ids, const int32_t* positions,
+                  int32_t n_tokens, const int32_t* page_table, int32_t batch, int32_t max_pages,
+                  void* kv_pages, int64_t num_pages, mlasd_stream_t stream) {
+  if (n_tokens < 0 || batch < 0) return MLASD_ERR_SHAPE;
+  if (n_tokens == 0) return MLASD_OK;
+  if (batch < 1 || max_pages < 1 || num_pages < 1) return MLASD_ERR_SHAPE;
+  if (!latent || !seq_ids || !positions || !page_table || !kv_pages) return MLASD_ERR_NULL;
+  if (!aligned(latent, 16) || !aligned(kv_pages, 16) || !aligned(seq_ids, 4) || !aligned(positions, 4) ||
+      !aligned(page_table, 4))
+    return MLASD_ERR_ALIGN;
+  int cus = 0;
+  int rc = device_cus(&cus);
+  if (rc != MLASD_OK) return rc;
+  mlasd::AppendParams p{};
+  p.latent = (const uint16_t*)latent;
+  p.seq_ids = seq_ids;
+  p.positions = positions;
+  p.n_tokens = n_tokens;
+  p.page_table = page_table;
+  p.batch = batch;
+  p.max_pages = max_pages;
+  p.kv = (uint8_t*)kv_pages;
+  p.num_pages = num_pages;
+  hipError_t e = mlasd::launch_append(p, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return MLASD_OK;
+}
+
 const char* mlasd_status_string(int status) {
   switch (status) {
     case MLASD_OK: return "ok";

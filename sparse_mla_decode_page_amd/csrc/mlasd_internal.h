@@ -58,8 +58,21 @@ struct GatherParams {
   int32_t split_len;
 };
 
+struct AppendParams {
+  const uint16_t* latent;     // bf16 [n_tokens, 512]: 448 nope, 64 rope
+  const int32_t* seq_ids;     // [n_tokens] page-table row of each token
+  const int32_t* positions;   // [n_tokens] position within its sequence
+  int32_t n_tokens;
+  const int32_t* page_table;  // [batch, max_pages]
+  int32_t batch;
+  int32_t max_pages;
+  uint8_t* kv;                // [num_pages, 149504]
+  int64_t num_pages;
+};
+
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_combine(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_gather(const GatherParams& p, hipStream_t stream);
+hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 
 }  // namespace mlasd

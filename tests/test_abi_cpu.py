@@ -26,7 +26,7 @@ def _declared_functions():
 def test_header_declares_entry_points():
     names = _declared_functions()
     for n in ("mla_sparse_decode", "mla_sparse_decode_ex", "mla_sparse_gather_dequant",
-              "mla_sparse_plan", "mlasd_status_string"):
+              "mla_sparse_plan", "mla_kv_append", "mlasd_status_string"):
         assert n in names
 
 
@@ -83,6 +83,24 @@ def test_gather_hook_validation_without_device():
     assert f(vp(0x1000), 1, vp(0x1000), 1, vp(0x1000), 4, vp(0x1000), 1, vp(0x1008), vp(0x1000),
              vp(0x1000), vp(0)) == -3
     assert f(vp(0x1000), 1, vp(0x1000), 1, vp(0x1000), 0, vp(0x1000), 1, vp(0), vp(0), vp(0), vp(0)) == 0
+
+
+def _append(lib, latent=0x1000, seq=0x1000, pos=0x1000, n=4, pt=0x1000, batch=1, max_pages=1,
+            kv=0x1000, num_pages=1):
+    vp = ctypes.c_void_p
+    return lib.mla_kv_append(vp(latent), vp(seq), vp(pos), n, vp(pt), batch, max_pages, vp(kv),
+                             num_pages, vp(0))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=-1), -2), (dict(batch=-1), -2), (dict(batch=0), -2), (dict(max_pages=0), -2),
+    (dict(num_pages=0), -2), (dict(latent=0), -1), (dict(seq=0), -1), (dict(pos=0), -1),
+    (dict(pt=0), -1), (dict(kv=0), -1), (dict(latent=0x1008), -3), (dict(kv=0x1008), -3),
+    (dict(pos=0x1002), -3), (dict(n=0), 0), (dict(n=0, latent=0, kv=0), 0),
+])
+def test_append_validation_without_device(kw, code):
+    lib = m.load_library()
+    assert _append(lib, **kw) == code
 
 
 @pytest.mark.parametrize("batch,topk,req,cus,expect", [
