@@ -79,7 +79,7 @@ def cpu_baseline(w, seconds):
                       f"numpy float64 with {threads} BLAS thread(s)"}
 
 
-def bench_append(dev, kv, pt, seq_len, steps, stream):
+def bench_append(dev, kv, pt, seq_len, steps, stream, traffic_json=None):
     """Time mla_kv_append writing the last `per_seq` positions of every
     sequence (a prefill-sized append of 4,096 tokens per sequence) into the
     resident pool; HIP events on the launch stream around `steps` calls."""
@@ -105,9 +105,15 @@ def bench_append(dev, kv, pt, seq_len, steps, stream):
     us = e0.elapsed_time(e1) * 1e3 / steps
     byts = n * APPEND_BYTES_PER_TOKEN
     gbs = byts / (us * 1e-6) / 1e9
+    traffic = None
+    if traffic_json and os.path.exists(traffic_json):
+        try:
+            traffic = json.load(open(traffic_json)).get(f"append_{B}x{per_seq}", {}).get("bytes_per_launch")
+        except Exception:
+            traffic = None
     return {"tokens_per_launch": n, "us_per_launch": us, "tokens_per_s": n / (us * 1e-6),
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
                          "algorithmic_bytes_per_launch": byts},
             "workload": f"{B} sequences x {per_seq} new tokens into the resident pool"}
 
@@ -173,7 +179,7 @@ def main():
         if int(w.seq_lens.min()) < 4096:
             print("--op append needs every sequence >= 4096 tokens (config 1-3)", file=sys.stderr)
             sys.exit(2)
-        res = bench_append(dev, kv, pt, int(w.seq_lens.min()), args.steps, side)
+        res = bench_append(dev, kv, pt, int(w.seq_lens.min()), args.steps, side, args.traffic_json)
         res["metric"] = "cache append: tokens/s"
         print(json.dumps(res), flush=True)
         return
@@ -299,7 +305,7 @@ def main():
     }
     if not args.no_append and int(w.seq_lens.min()) >= 4096:
         # runs after the decode timing: it overwrites the pool's tail records
-        res["kv_append"] = bench_append(dev, kv, pt, int(w.seq_lens.min()), 50, side)
+        res["kv_append"] = bench_append(dev, kv, pt, int(w.seq_lens.min()), 50, side, args.traffic_json)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

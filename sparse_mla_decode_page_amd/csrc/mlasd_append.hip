@@ -36,19 +36,22 @@ __global__ __launch_bounds__(64 * kAppendWaves) void mla_kv_append_kernel(const 
   const int lane = threadIdx.x & 63;
   const int tok = blockIdx.x * kAppendWaves + (threadIdx.x >> 6);
   if (tok >= p.n_tokens) return;   // wave-uniform
-  // validity (every lane reads the same words: wave-uniform)
+  // The latent row is issued first so its latency overlaps the dependent
+  // seq id -> page table lookups.  Lanes 0..55: 8 nope values; lanes 56..63:
+  // 8 rope values (bf16 bits).  Nothing here is read again: stream it.
+  const u32x4 w = __builtin_nontemporal_load((const u32x4*)(p.latent + (int64_t)tok * kDQK) + lane);
+  // Validity, wave-uniform and branch-free up to one exit so the compiler
+  // keeps the latent load above it: the page-table lookup is clamped to
+  // entry 0 (batch >= 1 and max_pages >= 1) when the token is out of range.
   const int s = p.seq_ids[tok], pos = p.positions[tok];
-  if (s < 0 || s >= p.batch || pos < 0) return;
-  const int lp = pos >> 8;
-  if (lp >= p.max_pages) return;
-  const int page = p.page_table[(int64_t)s * p.max_pages + lp];
+  const bool in_table = s >= 0 && s < p.batch && pos >= 0 && (pos >> 8) < p.max_pages;
+  const int64_t entry = in_table ? (int64_t)s * p.max_pages + (pos >> 8) : 0;
+  const int looked_up = p.page_table[entry];
+  const int page = in_table ? looked_up : -1;
   if (page < 0 || (int64_t)page >= p.num_pages) return;
   const int slot = pos & (kPageTokens - 1);
   uint8_t* pbase = p.kv + (int64_t)page * kPageBytes;
-  const uint16_t* src = p.latent + (int64_t)tok * kDQK;
 
-  // lanes 0..55: 8 nope values; lanes 56..63: 8 rope values (bf16 bits)
-  const u32x4 w = *(const u32x4*)(src + 8 * lane);
   float v[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -75,9 +78,9 @@ __global__ __launch_bounds__(64 * kAppendWaves) void mla_kv_append_kernel(const 
     hi = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[6], -k), ldexpf(v[7], -k), hi, true);
     codes.x = lo;
     codes.y = hi;
-    *(u32x2*)(pbase + slot * kRecordBytes + 8 * lane) = codes;
+    __builtin_nontemporal_store(codes, (u32x2*)(pbase + slot * kRecordBytes + 8 * lane));
   } else {
-    *(u32x4*)(pbase + slot * kRecordBytes + kDNope + 16 * (lane - kDNope / 8)) = w;
+    __builtin_nontemporal_store(w, (u32x4*)(pbase + slot * kRecordBytes + kDNope + 16 * (lane - kDNope / 8)));
   }
   // scale record: bytes 0..6 = k + 127 of groups 0..6 (lanes 0, 8, .., 48), byte 7 = 0
   uint32_t sb[7];
@@ -87,7 +90,7 @@ __global__ __launch_bounds__(64 * kAppendWaves) void mla_kv_append_kernel(const 
     u32x2 rec;
     rec.x = sb[0] | (sb[1] << 8) | (sb[2] << 16) | (sb[3] << 24);
     rec.y = sb[4] | (sb[5] << 8) | (sb[6] << 16);
-    *(u32x2*)(pbase + kScaleBase + slot * kScaleRecordBytes) = rec;
+    __builtin_nontemporal_store(rec, (u32x2*)(pbase + kScaleBase + slot * kScaleRecordBytes));
   }
 }
 
