@@ -33,7 +33,8 @@ What is computed (cited by page title and section):
   dequantised key.  The outputs are the attention values and a log-sum-exp
   per head ("The Validation Gate", "Output Knowledge Created", item 4).
 
-Readings where the pages are silent (each is listed in the design notes):
+Readings where the pages are silent (numbered as in the design notes, whose
+R7-R12 cover the output format, tolerances, record order and the kernel):
   R1  7 scale bytes per token, byte g scales nope dims [64g, 64g+64); byte 7
       is padding and is ignored.
   R2  UE8M0 byte e means 2^(e-127); e = 255 is NaN.
@@ -46,7 +47,7 @@ Readings where the pages are silent (each is listed in the design notes):
       Every valid entry counts once, duplicates included.
   R5  lse is the natural log of the sum of exp over the *scaled* scores.
   R6  A query with no valid entry gets out = 0 and lse = -inf.
-  R7  (cache append) A token latent is quantised per 64-dim group: the scale
+  R13 (cache append) A token latent is quantised per 64-dim group: the scale
       exponent k is the least integer with amax <= 448 * 2^k, clamped to
       [-127, 127] (amax = 0 gives -127); the scale byte is k + 127; every value
       is encoded as the e4m3 code nearest to x * 2^-k, ties to the even code,
@@ -219,7 +220,7 @@ def lse_combine(outs, lses):
 
 
 # ----------------------------------------------------------------------------
-# cache append: quantise token latents into records (reading R7)
+# cache append: quantise token latents into records (reading R13)
 # ----------------------------------------------------------------------------
 
 def scale_exponent(amax):
@@ -254,7 +255,7 @@ def e4m3_encode_nearest(y):
 
 def quantize_token(latent_bits):
     """One token latent (bf16 bits [512]: 448 nope, 64 rope) -> (the 576-byte
-    token record, the 8-byte scale record) (reading R7)."""
+    token record, the 8-byte scale record) (reading R13)."""
     bits = np.asarray(latent_bits, dtype=np.uint16)
     x = bf16_value(bits[:NOPE])
     rec = np.zeros(RECORD_BYTES, dtype=np.uint8)
@@ -270,7 +271,7 @@ def quantize_token(latent_bits):
 
 
 def kv_append(kv_pages, page_table, seq_ids, positions, latent_bits):
-    """A copy of the pool with every valid token written (reading R7)."""
+    """A copy of the pool with every valid token written (reading R13)."""
     kv = np.array(kv_pages, dtype=np.uint8, copy=True)
     pt = np.asarray(page_table, dtype=np.int64)
     B, max_pages = pt.shape

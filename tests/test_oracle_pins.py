@@ -326,7 +326,7 @@ def test_decimal_brute_force_tiny():
 
 
 # ----------------------------------------------------------------------------
-# cache append: the quantiser (reading R7)
+# cache append: the quantiser (reading R13)
 # ----------------------------------------------------------------------------
 
 @pytest.mark.parametrize("amax,k", [(448.0, 0), (449.0, 1), (224.0, -1), (224.5, 0), (1.0, -8),
