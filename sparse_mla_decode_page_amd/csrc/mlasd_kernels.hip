@@ -74,7 +74,9 @@ static_assert(2 * kStageBytes <= (int)sizeof(Smem::k[0]) && 2 * kStageBytes <= (
 __device__ __forceinline__ int logical_block(int n) {
   // Workgroups are dispatched round-robin over the 8 XCDs (block i -> XCD
   // i % 8).  Renumber so that consecutive logical blocks -- the slices of one
-  // query, which read the same Q -- run on the same XCD and share its L2.
+  // query, which read the same Q, and the combine's workgroups of that query,
+  // which read what the slices wrote -- run on the same XCD and share its L2.
+  // Each XCD gets one contiguous range of logical blocks, in proportion.
   const int i = blockIdx.x;
   const int xcd = i & 7, k = i >> 3;
   const int per = n >> 3, rem = n & 7;
@@ -443,7 +445,10 @@ constexpr int kCombineThreads = 128;   // one workgroup per (query, head); 112 f
 // memory round trip.  Weights: w_s = exp(lse_s - max) / sum; empty slices
 // (lse = -inf) get 0; a query with no valid entry gets out = 0, lse = -inf.
 __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(const DecodeParams p) {
-  const int b = blockIdx.x / kHeads, h = blockIdx.x - b * kHeads;
+  // Same query -> XCD placement as the decode kernel, whose slices of this
+  // query wrote the partials through this XCD's L2 just before.
+  const int lb = logical_block(p.batch * kHeads);
+  const int b = lb / kHeads, h = lb - b * kHeads;
   const int ns = p.nsplit;   // <= kMaxTopk / kTileTokens = 16
   const int c4 = threadIdx.x;
   const float* pl = p.part_lse + (int64_t)b * ns * kHeads + h;
