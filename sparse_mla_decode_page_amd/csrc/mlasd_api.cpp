@@ -84,10 +84,11 @@ int stream_workspace(hipStream_t stream, size_t bytes, void** out) {
 
 // Split plan: one workgroup per (query, top-k slice).  Without a request the
 // slices are sized so the grid covers every compute unit once, but no slice
-// is cut below kMinAutoSlice entries: a workgroup needs a few tiles for its
-// gather to overlap its contractions, and every extra slice costs a partial
-// write and read.  A slice holds a whole number of 32-token tiles.
-constexpr int kMinAutoSlice = 128;
+// is cut below kMinAutoSlice entries: every extra slice costs a partial
+// write and read, and below two tiles a workgroup's fixed start-up cost
+// (index resolution, first gather) dominates.  A slice holds a whole number
+// of 32-token tiles.
+constexpr int kMinAutoSlice = 64;
 
 void make_plan(int32_t batch, int32_t topk, int32_t request, int cus, int32_t* nsplit,
                int32_t* split_len) {

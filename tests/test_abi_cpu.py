@@ -105,18 +105,18 @@ def test_append_validation_without_device(kw, code):
 
 @pytest.mark.parametrize("batch,topk,req,cus,expect", [
     (64, 512, 0, 256, (4, 128)),     # one workgroup per compute unit
-    (1, 512, 0, 256, (4, 128)),      # small batch: slices of at least 128 entries
-    (16, 512, 0, 256, (4, 128)),
+    (1, 512, 0, 256, (8, 64)),       # small batch: slices of at least 64 entries
+    (16, 512, 0, 256, (8, 64)),
     (128, 512, 0, 256, (2, 256)),
     (256, 512, 0, 256, (1, 512)),    # batch fills the GPU: no split
     (1, 64, 0, 256, (1, 64)),
-    (3, 300, 0, 256, (3, 128)),      # ragged top-k
+    (3, 300, 0, 256, (5, 64)),       # ragged top-k
     (3, 45, 0, 256, (1, 64)),
     (1, 0, 0, 256, (1, 32)),         # empty top-k: one slice, writes zeros / -inf
     (64, 512, 1, 256, (1, 512)),     # forced
     (64, 512, 3, 256, (3, 192)),     # slices hold whole 32-token tiles
     (64, 512, 99, 256, (16, 32)),    # clamped to ceil(topk/32)
-    (8, 100, 0, 80, (1, 128)),
+    (8, 100, 0, 80, (2, 64)),
     (32, 512, 0, 80, (3, 192)),
 ])
 def test_plan(batch, topk, req, cus, expect):
