@@ -79,6 +79,49 @@ def cpu_baseline(w, seconds):
                       f"numpy float64 with {threads} BLAS thread(s)"}
 
 
+def copy_bandwidth(dev, mib=1024, reps=5):
+    """Device-to-device copy rate (read + write bytes per second): the
+    practical HBM ceiling on this GPU, reported beside the 8 TB/s peak."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / reps
+    del src, dst
+    return 2 * n / sec / 1e9
+
+
+def cold_calls(step, n_sets, stream, dev, calls=50, flush_mb=512):
+    """Per-call duration (HIP events on the launch stream) of single eager
+    calls, each after a flush write that evicts L2 and the Infinity Cache."""
+    import torch
+    flush = torch.empty(flush_mb << 18, dtype=torch.int32, device=dev)
+    times = []
+    with torch.cuda.stream(stream):
+        for i in range(calls):
+            flush.fill_(i)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step(i % n_sets, stream)
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3)
+    del flush
+    t = np.array(times)
+    return {"median_us": float(np.median(t)), "p10_us": float(np.percentile(t, 10)),
+            "p90_us": float(np.percentile(t, 90)), "calls": calls, "flush_mb": flush_mb,
+            "launch": "eager, one call per flush"}
+
+
 def bench_append(dev, kv, pt, seq_len, steps, stream, traffic_json=None):
     """Time mla_kv_append writing the last `per_seq` positions of every
     sequence (a prefill-sized append of 4,096 tokens per sequence) into the
@@ -249,6 +292,9 @@ def main():
         raise RuntimeError("graph replay output differs from the eager call")
     args.steps = steps_done
 
+    cold = cold_calls(step, n_sets, side, dev)
+    copy_gbs = copy_bandwidth(dev)
+
     order = [i % n_sets for i in range(args.steps)]
     attended = sum(stats[k]["attended"] for k in order) / args.steps
     byts = sum(stats[k]["bytes"] for k in order) / args.steps
@@ -287,6 +333,7 @@ def main():
             "nsplit": nsplit, "split_len": split_len, "input_sets": n_sets,
             "launch": "HIP graph replay (one graph = one pass over the input sets)",
             "eager_ms_per_step": eager_ms,
+            "cold_call": cold,
             "parallelism": "single GPU",
         },
         "roofline": {
@@ -296,6 +343,8 @@ def main():
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
+            "copy_gbs": copy_gbs,
+            "frac_of_copy": achieved / copy_gbs,
             "algorithmic_bytes_per_step": byts,
             "kv_gbs": kvb / sec / 1e9,
             "mfma_tflops": flops / sec / 1e12,

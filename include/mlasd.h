@@ -181,6 +181,33 @@ int mla_kv_append(const void* latent, const int32_t* seq_ids, const int32_t* pos
                   int32_t n_tokens, const int32_t* page_table, int32_t batch, int32_t max_pages,
                   void* kv_pages, int64_t num_pages, mlasd_stream_t stream);
 
+/*
+ * mlasd_prepare -- reserve the split scratch of `stream` (on the current
+ * device) for every automatically planned mla_sparse_decode call with
+ * batch <= max_batch and topk <= max_topk, so that such calls made later
+ * under graph capture allocate nothing.  Everything a captured call needs
+ * must exist before capture begins ("The Validation Moment", "The Weight of
+ * 'CUDA Graph Capture Completed Without Errors'").  Forced plans
+ * (mla_sparse_decode_ex) may need more.  Host call; may allocate and
+ * synchronise the stream; refused with MLASD_ERR_CAPTURE while the stream
+ * is capturing and the scratch would have to grow.  max_batch == 0 reserves
+ * nothing.  Errors: MLASD_ERR_SHAPE (negative sizes, max_topk > 512),
+ * MLASD_ERR_DEVICE, MLASD_ERR_HIP.
+ */
+int mlasd_prepare(mlasd_stream_t stream, int32_t max_batch, int32_t max_topk);
+
+/*
+ * mlasd_release -- synchronise `stream` and free its split scratch on the
+ * current device (a no-op if it has none).  Refused with MLASD_ERR_CAPTURE
+ * while the stream is capturing.  A later call reserves scratch again.
+ * Graphs captured while the freed scratch was in use must not be replayed
+ * afterwards.
+ */
+int mlasd_release(mlasd_stream_t stream);
+
+/* Bytes of split scratch currently held for `stream` on the current device. */
+int mlasd_workspace_bytes(mlasd_stream_t stream, size_t* bytes);
+
 /* Static text for a status code. */
 const char* mlasd_status_string(int status);
 

@@ -11,8 +11,11 @@ from ._binding import (  # noqa: F401
     mla_sparse_decode,
     mla_sparse_gather_dequant,
     plan,
+    prepare,
+    release,
     status_string,
+    workspace_bytes,
 )
 
-__all__ = ["mla_sparse_decode", "mla_sparse_gather_dequant", "mla_kv_append", "plan", "load_library",
-           "library_path", "status_string", "MlasdError"]
+__all__ = ["mla_sparse_decode", "mla_sparse_gather_dequant", "mla_kv_append", "plan", "prepare",
+           "release", "workspace_bytes", "load_library", "library_path", "status_string", "MlasdError"]

@@ -53,6 +53,12 @@ def load_library():
     lib.mla_sparse_gather_dequant.restype = ctypes.c_int
     lib.mla_kv_append.argtypes = [vp, vp, vp, i32, vp, i32, i32, vp, i64, vp]
     lib.mla_kv_append.restype = ctypes.c_int
+    lib.mlasd_prepare.argtypes = [vp, i32, i32]
+    lib.mlasd_prepare.restype = ctypes.c_int
+    lib.mlasd_release.argtypes = [vp]
+    lib.mlasd_release.restype = ctypes.c_int
+    lib.mlasd_workspace_bytes.argtypes = [vp, ctypes.POINTER(ctypes.c_size_t)]
+    lib.mlasd_workspace_bytes.restype = ctypes.c_int
     lib.mlasd_status_string.argtypes = [ctypes.c_int]
     lib.mlasd_status_string.restype = ctypes.c_char_p
     lib.mlasd_last_hip_error.argtypes = []
@@ -106,6 +112,34 @@ def plan(batch: int, topk: int, nsplit: int = 0, num_cus: int = 0):
     _check(lib.mla_sparse_plan(batch, topk, nsplit, num_cus, ctypes.byref(a), ctypes.byref(b)),
            "mla_sparse_plan")
     return a.value, b.value
+
+
+def prepare(max_batch: int, max_topk: int = MAX_TOPK, stream=None, device=None):
+    """Reserve the split scratch of `stream` for every automatically planned
+    decode with batch <= max_batch and topk <= max_topk (call before graph
+    capture)."""
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    lib = load_library()
+    with torch.cuda.device(dev):
+        _check(lib.mlasd_prepare(_stream(stream, dev), max_batch, max_topk), "mlasd_prepare")
+
+
+def release(stream=None, device=None):
+    """Free the split scratch of `stream` (synchronises the stream)."""
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    lib = load_library()
+    with torch.cuda.device(dev):
+        _check(lib.mlasd_release(_stream(stream, dev)), "mlasd_release")
+
+
+def workspace_bytes(stream=None, device=None) -> int:
+    """Bytes of split scratch the library holds for `stream`."""
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    with torch.cuda.device(dev):
+        _check(lib.mlasd_workspace_bytes(_stream(stream, dev), ctypes.byref(n)), "mlasd_workspace_bytes")
+    return n.value
 
 
 def _check_cache_args(kv_pages, page_table, topk_idx, seq_lens):

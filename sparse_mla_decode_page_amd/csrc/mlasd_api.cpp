@@ -111,6 +111,13 @@ void make_plan(int32_t batch, int32_t topk, int32_t request, int cus, int32_t* n
   *split_len = len;
 }
 
+// Bytes of split scratch for one call: fp32 partial rows, then fp32 lse values.
+size_t split_scratch_bytes(int32_t batch, int32_t nsplit) {
+  const size_t n_o = (size_t)batch * nsplit * mlasd::kHeads * mlasd::kDV;
+  const size_t n_l = (size_t)batch * nsplit * mlasd::kHeads;
+  return (n_o + n_l) * sizeof(float);
+}
+
 int check_common(const void* kv, int64_t num_pages, const int32_t* page_table, int32_t max_pages,
                  const int32_t* topk_idx, int32_t topk, const int32_t* seq_lens, int32_t batch) {
   if (batch < 0 || topk < 0 || topk > MLASD_MAX_TOPK) return MLASD_ERR_SHAPE;
@@ -155,9 +162,8 @@ int decode_impl(const void* q, const void* kv_pages, int64_t num_pages, const in
 
   if (p.nsplit > 1) {
     const size_t n_o = (size_t)batch * p.nsplit * mlasd::kHeads * mlasd::kDV;
-    const size_t n_l = (size_t)batch * p.nsplit * mlasd::kHeads;
     void* scratch = nullptr;
-    rc = stream_workspace(stream, (n_o + n_l) * sizeof(float), &scratch);
+    rc = stream_workspace(stream, split_scratch_bytes(batch, p.nsplit), &scratch);
     if (rc != MLASD_OK) return rc;
     p.part_o = (float*)scratch;
     p.part_lse = (float*)scratch + n_o;
@@ -256,6 +262,55 @@ int mla_kv_append(const void* latent, const int32_t* seq_ids, const int32_t* pos
   p.num_pages = num_pages;
   hipError_t e = mlasd::launch_append(p, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e);
+  return MLASD_OK;
+}
+
+int mlasd_prepare(mlasd_stream_t stream_, int32_t max_batch, int32_t max_topk) {
+  if (max_batch < 0 || max_topk < 0 || max_topk > MLASD_MAX_TOPK) return MLASD_ERR_SHAPE;
+  int cus = 0;
+  int rc = device_cus(&cus);
+  if (rc != MLASD_OK) return rc;
+  // The automatic plan's slice count grows with topk, so planning at
+  // max_topk for every batch size up to max_batch bounds every call.
+  size_t need = 0;
+  for (int32_t b = 1; b <= max_batch; ++b) {
+    int32_t ns = 1, len = 0;
+    make_plan(b, max_topk, 0, cus, &ns, &len);
+    if (ns > 1 && split_scratch_bytes(b, ns) > need) need = split_scratch_bytes(b, ns);
+  }
+  if (need == 0) return MLASD_OK;
+  void* scratch = nullptr;
+  return stream_workspace((hipStream_t)stream_, need, &scratch);
+}
+
+int mlasd_release(mlasd_stream_t stream_) {
+  hipStream_t stream = (hipStream_t)stream_;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  auto it = g_ws.find({dev, stream});
+  if (it == g_ws.end() || it->second.ptr == nullptr) return MLASD_OK;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  e = hipStreamIsCapturing(stream, &cs);
+  if (e != hipSuccess) return hip_fail(e);
+  if (cs != hipStreamCaptureStatusNone) return MLASD_ERR_CAPTURE;
+  e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e);
+  e = hipFree(it->second.ptr);
+  g_ws.erase(it);
+  if (e != hipSuccess) return hip_fail(e);
+  return MLASD_OK;
+}
+
+int mlasd_workspace_bytes(mlasd_stream_t stream_, size_t* bytes) {
+  if (bytes == nullptr) return MLASD_ERR_NULL;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  auto it = g_ws.find({dev, (hipStream_t)stream_});
+  *bytes = it == g_ws.end() ? 0 : it->second.bytes;
   return MLASD_OK;
 }
 

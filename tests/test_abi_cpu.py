@@ -26,7 +26,8 @@ def _declared_functions():
 def test_header_declares_entry_points():
     names = _declared_functions()
     for n in ("mla_sparse_decode", "mla_sparse_decode_ex", "mla_sparse_gather_dequant",
-              "mla_sparse_plan", "mla_kv_append", "mlasd_status_string"):
+              "mla_sparse_plan", "mla_kv_append", "mlasd_prepare", "mlasd_release",
+              "mlasd_workspace_bytes", "mlasd_status_string"):
         assert n in names
 
 
@@ -83,6 +84,15 @@ def test_gather_hook_validation_without_device():
     assert f(vp(0x1000), 1, vp(0x1000), 1, vp(0x1000), 4, vp(0x1000), 1, vp(0x1008), vp(0x1000),
              vp(0x1000), vp(0)) == -3
     assert f(vp(0x1000), 1, vp(0x1000), 1, vp(0x1000), 0, vp(0x1000), 1, vp(0), vp(0), vp(0), vp(0)) == 0
+
+
+def test_prepare_validation_without_device():
+    lib = m.load_library()
+    vp = ctypes.c_void_p
+    assert lib.mlasd_prepare(vp(0), -1, 512) == -2
+    assert lib.mlasd_prepare(vp(0), 4, 513) == -2
+    assert lib.mlasd_prepare(vp(0), 4, -1) == -2
+    assert lib.mlasd_workspace_bytes(vp(0), None) == -1
 
 
 def _append(lib, latent=0x1000, seq=0x1000, pos=0x1000, n=4, pt=0x1000, batch=1, max_pages=1,

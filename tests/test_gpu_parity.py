@@ -286,6 +286,45 @@ def test_graph_capture_replay():
         torch.cuda.synchronize()
 
 
+def test_prepare_capture_release():
+    """mlasd_prepare reserves a stream's split scratch, so a first split call
+    made under graph capture allocates nothing; without it the growth is
+    refused before anything is enqueued; mlasd_release frees the scratch."""
+    w, (ref_out, ref_lse) = config(3)   # B=64, topk=512: planned split
+    assert mlasd.plan(w.batch, w.topk)[0] > 1
+    d = to_device(w)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    out = torch.empty((w.batch, 64, 448), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.batch, 64), dtype=torch.float32, device="cuda")
+    assert mlasd.workspace_bytes(stream=s) == 0
+    g0 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g0, stream=s):
+        out.zero_()
+        with pytest.raises(mlasd.MlasdError, match="capturing"):
+            mlasd.mla_sparse_decode(d["q"], d["kv_pages"], d["page_table"], d["topk_idx"],
+                                    d["seq_lens"], w.softmax_scale, out=out, lse=lse, stream=s)
+    del g0
+    mlasd.prepare(w.batch, w.topk, stream=s)
+    ns = mlasd.plan(w.batch, w.topk)[0]
+    assert mlasd.workspace_bytes(stream=s) >= w.batch * ns * 64 * 449 * 4
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        mlasd.mla_sparse_decode(d["q"], d["kv_pages"], d["page_table"], d["topk_idx"],
+                                d["seq_lens"], w.softmax_scale, out=out, lse=lse, stream=s)
+    for rep in range(2):
+        out.zero_()
+        lse.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        check_attention(out, lse, ref_out, ref_lse, label=f"prepared capture, replay {rep}")
+    del g
+    mlasd.release(stream=s)
+    assert mlasd.workspace_bytes(stream=s) == 0
+    mlasd.release(stream=s)   # nothing held: no-op
+
+
 def test_split_merge_alternating_inputs():
     """The fused LSE merge reads partials written by other workgroups of the
     same launch: alternate two input sets of one shape on one stream, with no
