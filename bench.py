@@ -178,6 +178,8 @@ def main():
     ap.add_argument("--op", choices=["decode", "append"], default="decode",
                     help="append: time only the cache-append kernel")
     ap.add_argument("--no-append", action="store_true", help="skip the cache-append measurement")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the flushed single-call timing and the copy ceiling (profiling runs)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 8 plain device-to-device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -234,7 +236,7 @@ def main():
             out=torch.empty((w.batch, 64, 448), dtype=torch.bfloat16, device=dev),
             lse=torch.empty((w.batch, 64), dtype=torch.float32, device=dev)))
     stats = [workload_stats(s) for s in sets]
-    nsplit, split_len = mlasd.plan(w.batch, w.topk, args.nsplit)
+    nsplit, split_len, head_groups = mlasd.plan(w.batch, w.topk, args.nsplit)
     nsplit_arg = args.nsplit if args.nsplit > 0 else None
 
     def step(i, stream):
@@ -292,8 +294,8 @@ def main():
         raise RuntimeError("graph replay output differs from the eager call")
     args.steps = steps_done
 
-    cold = cold_calls(step, n_sets, side, dev)
-    copy_gbs = copy_bandwidth(dev)
+    cold = None if args.no_cold else cold_calls(step, n_sets, side, dev)
+    copy_gbs = None if args.no_cold else copy_bandwidth(dev)
 
     order = [i % n_sets for i in range(args.steps)]
     attended = sum(stats[k]["attended"] for k in order) / args.steps
@@ -307,7 +309,7 @@ def main():
     if os.path.exists(args.traffic_json):
         try:
             tj = json.load(open(args.traffic_json))
-            key = f"config{args.config}_nsplit{nsplit}"
+            key = f"config{args.config}_nsplit{nsplit}_hg{head_groups}"
             if key in tj:
                 traffic = tj[key]["bytes_per_launch"]
         except Exception:
@@ -330,7 +332,8 @@ def main():
             "workload": CONFIG_NAMES[args.config],
             "batch": w.batch, "heads": 64, "topk": w.topk,
             "valid_entries_per_step": stats[0]["n_valid"],
-            "nsplit": nsplit, "split_len": split_len, "input_sets": n_sets,
+            "nsplit": nsplit, "split_len": split_len, "head_groups": head_groups,
+            "input_sets": n_sets,
             "launch": "HIP graph replay (one graph = one pass over the input sets)",
             "eager_ms_per_step": eager_ms,
             "cold_call": cold,
@@ -344,7 +347,7 @@ def main():
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
             "copy_gbs": copy_gbs,
-            "frac_of_copy": achieved / copy_gbs,
+            "frac_of_copy": achieved / copy_gbs if copy_gbs else None,
             "algorithmic_bytes_per_step": byts,
             "kv_gbs": kvb / sec / 1e9,
             "mfma_tflops": flops / sec / 1e12,

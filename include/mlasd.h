@@ -106,12 +106,19 @@ int mla_sparse_decode(const void* q,
                       mlasd_stream_t stream);
 
 /*
- * mla_sparse_decode_ex -- mla_sparse_decode with the split plan forced:
- * the top-k list of each query is cut into `nsplit` slices handled by
- * separate workgroups and merged by the LSE combine ("The Turning Point",
- * Step 5).  nsplit <= 0 selects the automatic plan; larger values are
- * clamped to ceil(topk / 32).  Results equal mla_sparse_decode's up to
- * floating-point rounding.  Intended for tests and benchmarks.
+ * mla_sparse_decode_ex -- mla_sparse_decode with the plan forced:
+ *   nsplit       the top-k list of each query is cut into `nsplit` slices
+ *                handled by separate workgroups and merged by the LSE
+ *                combine ("The Turning Point", Step 5).  <= 0: automatic;
+ *                larger values are clamped to ceil(topk / 32).
+ *   head_groups  1: each workgroup computes all 64 heads of its slice (the
+ *                pages' one-program-per-query layout, Steps 3-4); 2: two
+ *                workgroups of 32 heads each share the slice's gathered
+ *                records.  0: automatic for the chosen nsplit.  Other values:
+ *                MLASD_ERR_SHAPE.
+ * Results equal mla_sparse_decode's up to floating-point rounding (the head
+ * groups do not change any value; the slices change the summation order).
+ * Intended for tests and benchmarks.
  */
 int mla_sparse_decode_ex(const void* q,
                          const void* kv_pages, int64_t num_pages,
@@ -120,18 +127,19 @@ int mla_sparse_decode_ex(const void* q,
                          const int32_t* seq_lens, int32_t batch,
                          float softmax_scale,
                          void* out, float* lse,
-                         int32_t nsplit,
+                         int32_t nsplit, int32_t head_groups,
                          mlasd_stream_t stream);
 
 /*
- * mla_sparse_plan -- the split plan the library would use (host only, no
- * device work): writes the number of top-k slices per query and the number
- * of index entries per slice (a multiple of 32).  nsplit_request as in
+ * mla_sparse_plan -- the plan the library would use (host only, no device
+ * work): writes the number of top-k slices per query, the number of index
+ * entries per slice (a multiple of 32) and, if head_groups is not NULL, the
+ * number of head groups (1 or 2).  nsplit_request as in
  * mla_sparse_decode_ex.  num_cus > 0 plans for that many compute units;
  * num_cus <= 0 queries the current HIP device.
  */
 int mla_sparse_plan(int32_t batch, int32_t topk, int32_t nsplit_request, int32_t num_cus,
-                    int32_t* nsplit, int32_t* split_len);
+                    int32_t* nsplit, int32_t* split_len, int32_t* head_groups);
 
 /*
  * mla_sparse_gather_dequant -- test hook for the gather + dequant stage:

@@ -45,9 +45,10 @@ def load_library():
     common = [vp, vp, i64, vp, i32, vp, i32, vp, i32, f32, vp, vp]
     lib.mla_sparse_decode.argtypes = common + [vp]
     lib.mla_sparse_decode.restype = ctypes.c_int
-    lib.mla_sparse_decode_ex.argtypes = common + [i32, vp]
+    lib.mla_sparse_decode_ex.argtypes = common + [i32, i32, vp]
     lib.mla_sparse_decode_ex.restype = ctypes.c_int
-    lib.mla_sparse_plan.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.mla_sparse_plan.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                    ctypes.POINTER(i32)]
     lib.mla_sparse_plan.restype = ctypes.c_int
     lib.mla_sparse_gather_dequant.argtypes = [vp, i64, vp, i32, vp, i32, vp, i32, vp, vp, vp, vp]
     lib.mla_sparse_gather_dequant.restype = ctypes.c_int
@@ -106,12 +107,12 @@ def _stream(stream, device):
 
 
 def plan(batch: int, topk: int, nsplit: int = 0, num_cus: int = 0):
-    """(nsplit, split_len) the library uses for this shape."""
+    """(nsplit, split_len, head_groups) the library uses for this shape."""
     lib = load_library()
-    a, b = ctypes.c_int32(0), ctypes.c_int32(0)
-    _check(lib.mla_sparse_plan(batch, topk, nsplit, num_cus, ctypes.byref(a), ctypes.byref(b)),
-           "mla_sparse_plan")
-    return a.value, b.value
+    a, b, c = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(lib.mla_sparse_plan(batch, topk, nsplit, num_cus, ctypes.byref(a), ctypes.byref(b),
+                               ctypes.byref(c)), "mla_sparse_plan")
+    return a.value, b.value, c.value
 
 
 def prepare(max_batch: int, max_topk: int = MAX_TOPK, stream=None, device=None):
@@ -160,12 +161,13 @@ def _check_cache_args(kv_pages, page_table, topk_idx, seq_lens):
 
 
 def mla_sparse_decode(q, kv_pages, page_table, topk_idx, seq_lens, softmax_scale,
-                      out=None, lse=None, stream=None, nsplit=None):
+                      out=None, lse=None, stream=None, nsplit=None, head_groups=None):
     """Sparse MLA decode.  Returns (out bf16 [B,64,448], lse f32 [B,64]).
 
     q bf16 [B,64,512]; kv_pages uint8 [num_pages,149504]; page_table int32
     [B,max_pages]; topk_idx int32 [B,topk]; seq_lens int32 [B].  `nsplit`
-    forces the number of top-k slices per query (None = library plan).
+    forces the number of top-k slices per query and `head_groups` (1 or 2)
+    the number of workgroups sharing a slice's heads (None = library plan).
     """
     B = _check_cache_args(kv_pages, page_table, topk_idx, seq_lens)
     _need(q, "q", torch.bfloat16, 3)
@@ -185,10 +187,11 @@ def mla_sparse_decode(q, kv_pages, page_table, topk_idx, seq_lens, softmax_scale
         args = (_ptr(q), _ptr(kv_pages), kv_pages.shape[0], _ptr(page_table), page_table.shape[1],
                 _ptr(topk_idx), topk_idx.shape[1], _ptr(seq_lens), B, float(softmax_scale),
                 _ptr(out), _ptr(lse))
-        if nsplit is None:
+        if nsplit is None and head_groups is None:
             rc = lib.mla_sparse_decode(*args, _stream(stream, dev))
         else:
-            rc = lib.mla_sparse_decode_ex(*args, int(nsplit), _stream(stream, dev))
+            rc = lib.mla_sparse_decode_ex(*args, int(nsplit or 0), int(head_groups or 0),
+                                          _stream(stream, dev))
     _check(rc, "mla_sparse_decode")
     return out, lse
 

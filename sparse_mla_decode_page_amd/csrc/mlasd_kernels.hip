@@ -231,11 +231,17 @@ __device__ __forceinline__ void store_tile(Smem& sm, const TileRegs& r, int buf,
 // a1-a7: main decode kernel
 // ---------------------------------------------------------------------------
 
+// kHeadGroups = 1: a workgroup computes all 64 heads of its (query, slice);
+// 2: 32 heads, with consumer waves 2..3 idle, for batches too small to fill
+// the GPU with slices alone.  The two head groups of a slice run on one XCD
+// and share its gathered records through L2.
+template <int kHeadGroups>
 __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeParams p) {
   __shared__ Smem sm;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int blk = logical_block(p.batch * p.nsplit);
-  const int b = blk / p.nsplit, s = blk - b * p.nsplit;
+  const int blk = logical_block(p.batch * p.nsplit * kHeadGroups);
+  const int hg = blk % kHeadGroups, bs = blk / kHeadGroups;
+  const int b = bs / p.nsplit, s = bs - b * p.nsplit;
   const int e0 = s * p.split_len;
   const int n_ent = max(0, min(p.topk - e0, p.split_len));
 
@@ -279,9 +285,15 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
   }
 
   // ---------------- consumers: a4 - a7 ----------------
+  constexpr int kActive = kConsumers / kHeadGroups;   // consumer waves with heads
+  if (wid >= kActive) {   // spare consumer waves only pass the barriers
+    for (int t = 0; t <= ntiles; ++t) __syncthreads();
+    return;
+  }
   const int g = lane >> 4;         // MFMA lane group
   const int col = lane & 15;       // MFMA column: head within the wave's 16
-  const int head = 16 * wid + col;
+  const int head0 = kHeads / kHeadGroups * hg + 16 * wid;   // the wave's first head
+  const int head = head0 + col;
 
   // Q^T operand for the wave's 16 heads, kept in registers: dims [32k + 8g, +8).
   bf16x8 qreg[16];
@@ -409,7 +421,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
       w.y = bf16x2_rne(oacc[mb][2] * inv, oacc[mb][3] * inv);
       *(u32x2*)(stage + col * kStageRowBytes + 2 * (16 * mb + 4 * g)) = w;
     }
-    uint8_t* obase = (uint8_t*)(p.out + ((int64_t)b * kHeads + 16 * wid) * kDV);
+    uint8_t* obase = (uint8_t*)(p.out + ((int64_t)b * kHeads + head0) * kDV);
 #pragma unroll
     for (int k = 0; k < 14; ++k) {   // 16 rows x 896 B = 14 x 1 KB
       const int i = lane + 64 * k, row = i / 56, ch = i - 56 * row;
@@ -417,7 +429,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
     }
     if (g == 0) p.lse[(int64_t)b * kHeads + head] = lse_v;
   } else {
-    const int64_t prow0 = ((int64_t)b * p.nsplit + s) * kHeads + 16 * wid;
+    const int64_t prow0 = ((int64_t)b * p.nsplit + s) * kHeads + head0;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {   // fp32 partials, 224 dims per pass
 #pragma unroll
@@ -541,8 +553,11 @@ __global__ __launch_bounds__(kThreads, 1) void mla_gather_kernel(const GatherPar
 // ---------------------------------------------------------------------------
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
-  const int nblk = p.batch * p.nsplit;
-  hipLaunchKernelGGL(mla_decode_kernel, dim3(nblk), dim3(kThreads), 0, stream, p);
+  const int nblk = p.batch * p.nsplit * p.head_groups;
+  if (p.head_groups == 2)
+    hipLaunchKernelGGL(mla_decode_kernel<2>, dim3(nblk), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(mla_decode_kernel<1>, dim3(nblk), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -50,13 +50,13 @@ def test_status_strings():
 
 
 def _decode(lib, q=0x1000, kv=0x1000, num_pages=1, pt=0x1000, max_pages=1, idx=0x1000, topk=4,
-            lens=0x1000, batch=1, scale=0.1, out=0x1000, lse=0x1000, nsplit=None):
+            lens=0x1000, batch=1, scale=0.1, out=0x1000, lse=0x1000, nsplit=None, hg=0):
     vp = ctypes.c_void_p
     args = (vp(q), vp(kv), num_pages, vp(pt), max_pages, vp(idx), topk, vp(lens), batch, scale,
             vp(out), vp(lse))
     if nsplit is None:
         return lib.mla_sparse_decode(*args, vp(0))
-    return lib.mla_sparse_decode_ex(*args, nsplit, vp(0))
+    return lib.mla_sparse_decode_ex(*args, nsplit, hg, vp(0))
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -66,7 +66,7 @@ def _decode(lib, q=0x1000, kv=0x1000, num_pages=1, pt=0x1000, max_pages=1, idx=0
     (dict(q=0x1008), -3), (dict(kv=0x1004), -3), (dict(out=0x1004), -3), (dict(lse=0x1002), -3),
     (dict(idx=0x1002), -3), (dict(scale=float("nan")), -4), (dict(scale=float("inf")), -4),
     (dict(batch=0), 0), (dict(batch=0, q=0, out=0, lse=0), 0),
-    (dict(topk=600, nsplit=2), -2),
+    (dict(topk=600, nsplit=2), -2), (dict(nsplit=2, hg=3), -2), (dict(nsplit=0, hg=-1), -2),
 ])
 def test_host_validation_without_device(kw, code):
     lib = m.load_library()
@@ -114,22 +114,27 @@ def test_append_validation_without_device(kw, code):
 
 
 @pytest.mark.parametrize("batch,topk,req,cus,expect", [
-    (64, 512, 0, 256, (4, 128)),     # one workgroup per compute unit
-    (1, 512, 0, 256, (8, 64)),       # small batch: slices of at least 64 entries
-    (16, 512, 0, 256, (8, 64)),
-    (128, 512, 0, 256, (2, 256)),
-    (256, 512, 0, 256, (1, 512)),    # batch fills the GPU: no split
-    (1, 64, 0, 256, (1, 64)),
-    (3, 300, 0, 256, (5, 64)),       # ragged top-k
-    (3, 45, 0, 256, (1, 64)),
-    (1, 0, 0, 256, (1, 32)),         # empty top-k: one slice, writes zeros / -inf
-    (64, 512, 1, 256, (1, 512)),     # forced
-    (64, 512, 3, 256, (3, 192)),     # slices hold whole 32-token tiles
-    (64, 512, 99, 256, (16, 32)),    # clamped to ceil(topk/32)
-    (8, 100, 0, 80, (2, 64)),
-    (32, 512, 0, 80, (3, 192)),
+    (64, 512, 0, 256, (2, 256, 2)),    # 4 workgroups per query: 2 slices x 2 head groups
+    (1, 512, 0, 256, (8, 64, 2)),      # small batch: slices of at least 64 entries
+    (16, 512, 0, 256, (8, 64, 2)),
+    (32, 512, 0, 256, (4, 128, 2)),
+    (128, 512, 0, 256, (1, 512, 2)),   # 2 workgroups per query: head groups, no split
+    (100, 512, 0, 256, (1, 512, 2)),
+    (129, 512, 0, 256, (1, 512, 1)),   # batch fills the GPU: 64 heads, no split
+    (256, 512, 0, 256, (1, 512, 1)),
+    (1, 64, 0, 256, (1, 64, 2)),
+    (3, 300, 0, 256, (5, 64, 2)),      # ragged top-k
+    (3, 45, 0, 256, (1, 64, 2)),
+    (1, 0, 0, 256, (1, 32, 2)),        # empty top-k: one slice, writes zeros / -inf
+    (64, 512, 1, 256, (1, 512, 2)),    # forced
+    (64, 512, 3, 256, (3, 192, 1)),    # slices hold whole 32-token tiles
+    (64, 512, 99, 256, (16, 32, 1)),   # clamped to ceil(topk/32)
+    (8, 100, 0, 80, (2, 64, 2)),
+    (32, 512, 0, 80, (1, 512, 2)),
 ])
 def test_plan(batch, topk, req, cus, expect):
-    ns, sl = m.plan(batch, topk, req, cus)
-    assert (ns, sl) == expect
+    ns, sl, hg = m.plan(batch, topk, req, cus)
+    assert (ns, sl, hg) == expect
     assert sl % 32 == 0 and ns * sl >= topk and (ns - 1) * sl < max(topk, 1)
+    if req == 0:
+        assert batch * ns * hg <= max(cus, batch)   # one round of workgroups
