@@ -89,6 +89,23 @@ __device__ __forceinline__ uint32_t pack2(V2 v) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Reductions over the 4 lane groups of a column (lanes l, l^16, l^32, l^48)
+// with VALU lane swaps: each swap leaves a lane its own value and its
+// partner's, so no LDS round trip is needed.
+__device__ __forceinline__ float group_max4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float group_sum4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
   const bf16x2 r = {(__bf16)a, (__bf16)b};   // v_cvt_pk_bf16_f32, round to nearest even
   return pack2(r);
@@ -344,8 +361,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
         x[mb][r] = ok ? sacc[mb][r] * p.scale_log2 : -INFINITY;
         tmax = fmaxf(tmax, x[mb][r]);
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax = group_max4(tmax);
     // Lazy rescale: O and l keep a reference max m_run; they are rescaled only
     // when some head of the wave sees its max rise by more than kRescaleLog2,
     // so P = exp2(x - m_run) stays <= 2^kRescaleLog2 (exact in fp16 range).
@@ -369,8 +385,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
         rsum += e;
         pb[4 * mb + r] = (_Float16)e;
       }
-    rsum += __shfl_xor(rsum, 16);
-    rsum += __shfl_xor(rsum, 32);
+    rsum = group_sum4(rsum);
     l_run += rsum;
 
     // a6: O^T[dim][head] += V^T P^T over the tile's 32 k-slots; the V^T
