@@ -53,7 +53,7 @@ constexpr int kDepth = 2;           // tiles gathered ahead by the producers
 constexpr int kTokPerProducer = kTileTokens / (kWaves - kConsumers);   // 8
 constexpr float kRescaleLog2 = 8.f; // lazy-rescale threshold (P <= 256)
 constexpr int kPvAhead = 3;         // PV operand blocks read ahead
-constexpr int kQkAhead = 2;         // QK^T operand k-steps read ahead
+constexpr int kQkAhead = 3;         // QK^T operand k-steps read ahead
 constexpr int kStageRowBytes = 912; // epilogue staging row: 896 B (+16 B pad)
 constexpr int kStageBytes = 16 * kStageRowBytes;   // one wave's 16 rows
 
@@ -347,6 +347,21 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
       for (int mb = 0; mb < 2; ++mb)
         sc[mb][k & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[k % (kQkAhead + 1)][mb], qreg[k], sc[mb][k & 1], 0, 0, 0);
     }
+    if constexpr (kHeadGroups == 2) {
+      // Two consumer waves per CU leave LDS bandwidth to spare, but under
+      // register pressure the compiler issues each K read just before its
+      // MFMA and waits out the LDS latency.  Pin the order: the prologue
+      // reads, then per k-step the reads of step k + kQkAhead before the two
+      // MFMAs of step k.  (With four consumer waves LDS bandwidth is the
+      // limit and this order is slower, so the 64-head kernel keeps the
+      // compiler's.)
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kQkAhead, 0);   // DS reads
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        if (k + kQkAhead < 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);            // MFMAs
+      }
+    }
     const f32x4 sacc[2] = {sc[0][0] + sc[0][1], sc[1][0] + sc[1][1]};
 
     // a5: online softmax.  Lane holds tokens 16mb + 4g + r of head `head`.
@@ -412,6 +427,14 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
       const f16x4 hi = __builtin_bit_cast(f16x4, vhi[mb % (kPvAhead + 1)]);
       const f16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       oacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb, oacc[mb], 0, 0, 0);
+    }
+    if constexpr (kHeadGroups == 2) {   // same for the V reads: kPvAhead blocks ahead
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPvAhead, 1);
+#pragma unroll
+      for (int mb = 0; mb < 28; ++mb) {
+        if (mb + kPvAhead < 28) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      }
     }
     __syncthreads();
   }
