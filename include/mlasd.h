@@ -112,10 +112,10 @@ int mla_sparse_decode(const void* q,
  *                combine ("The Turning Point", Step 5).  <= 0: automatic;
  *                larger values are clamped to ceil(topk / 32).
  *   head_groups  1: each workgroup computes all 64 heads of its slice (the
- *                pages' one-program-per-query layout, Steps 3-4); 2: two
- *                workgroups of 32 heads each share the slice's gathered
- *                records.  0: automatic for the chosen nsplit.  Other values:
- *                MLASD_ERR_SHAPE.
+ *                pages' one-program-per-query layout, Steps 3-4); 2 or 4:
+ *                that many workgroups of 32 or 16 heads share the slice's
+ *                gathered records.  0: automatic for the chosen nsplit.
+ *                Other values: MLASD_ERR_SHAPE.
  * Results equal mla_sparse_decode's up to floating-point rounding (the head
  * groups do not change any value; the slices change the summation order).
  * Intended for tests and benchmarks.
@@ -134,7 +134,7 @@ int mla_sparse_decode_ex(const void* q,
  * mla_sparse_plan -- the plan the library would use (host only, no device
  * work): writes the number of top-k slices per query, the number of index
  * entries per slice (a multiple of 32) and, if head_groups is not NULL, the
- * number of head groups (1 or 2).  nsplit_request as in
+ * number of head groups (1, 2 or 4).  nsplit_request as in
  * mla_sparse_decode_ex.  num_cus > 0 plans for that many compute units;
  * num_cus <= 0 queries the current HIP device.
  */

@@ -166,7 +166,7 @@ def mla_sparse_decode(q, kv_pages, page_table, topk_idx, seq_lens, softmax_scale
 
     q bf16 [B,64,512]; kv_pages uint8 [num_pages,149504]; page_table int32
     [B,max_pages]; topk_idx int32 [B,topk]; seq_lens int32 [B].  `nsplit`
-    forces the number of top-k slices per query and `head_groups` (1 or 2)
+    forces the number of top-k slices per query and `head_groups` (1, 2, 4)
     the number of workgroups sharing a slice's heads (None = library plan).
     """
     B = _check_cache_args(kv_pages, page_table, topk_idx, seq_lens)

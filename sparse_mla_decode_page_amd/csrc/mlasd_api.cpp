@@ -90,7 +90,9 @@ int stream_workspace(hipStream_t stream, size_t bytes, void** out) {
 //     instead of four and loads half of Q, and its sibling shares the
 //     gathered records through L2 (measured: c1 12.8 -> 11.2 us, c2 15.6 ->
 //     13.9 us, c3 with 2 slices of 32-head groups 23.8 us against 24.9 us
-//     with 4 slices of 64 heads);
+//     with 4 slices of 64 heads); when most CUs would still idle (B <= 2 at
+//     topk 512), four head groups of 16 heads (c0 6.95 -> 6.3 us, c1 10.6 ->
+//     10.1 us);
 //   - the rest of the budget in top-k slices, none cut below kMinAutoSlice
 //     entries: every extra slice costs a partial write and read, and below
 //     two tiles a workgroup's fixed start-up cost (index resolution, first
@@ -120,6 +122,8 @@ void make_plan(int32_t batch, int32_t topk, int32_t ns_request, int32_t hg_reque
   *split_len = len;
   if (hg_request > 0)
     *head_groups = hg_request;
+  else if ((int64_t)batch * ns * 4 <= cus / 4)
+    *head_groups = 4;   // most CUs would idle: 16-head workgroups (B <= 2 at topk 512)
   else
     *head_groups = (int64_t)batch * ns * 2 <= cus ? 2 : 1;
 }
@@ -151,7 +155,7 @@ int decode_impl(const void* q, const void* kv_pages, int64_t num_pages, const in
   int rc = check_common(kv_pages, num_pages, page_table, max_pages, topk_idx, topk, seq_lens, batch);
   if (rc != MLASD_OK) return rc;
   if (!std::isfinite(softmax_scale)) return MLASD_ERR_VALUE;
-  if (hg_req < 0 || hg_req > 2) return MLASD_ERR_SHAPE;
+  if (hg_req < 0 || hg_req > 4 || hg_req == 3) return MLASD_ERR_SHAPE;
   if (batch == 0) return MLASD_OK;
   if (!q || !out || !lse) return MLASD_ERR_NULL;
   if (!aligned(q, 16) || !aligned(out, 8) || !aligned(lse, 4)) return MLASD_ERR_ALIGN;

@@ -249,9 +249,10 @@ __device__ __forceinline__ void store_tile(Smem& sm, const TileRegs& r, int buf,
 // ---------------------------------------------------------------------------
 
 // kHeadGroups = 1: a workgroup computes all 64 heads of its (query, slice);
-// 2: 32 heads, with consumer waves 2..3 idle, for batches too small to fill
-// the GPU with slices alone.  The two head groups of a slice run on one XCD
-// and share its gathered records through L2.
+// 2: 32 heads, with consumer waves 2..3 idle; 4: 16 heads, with consumer
+// waves 1..3 idle -- for batches too small to fill the GPU with slices alone.
+// The head groups of a slice run on one XCD and share its gathered records
+// through L2.
 template <int kHeadGroups>
 __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeParams p) {
   __shared__ Smem sm;
@@ -347,8 +348,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
       for (int mb = 0; mb < 2; ++mb)
         sc[mb][k & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[k % (kQkAhead + 1)][mb], qreg[k], sc[mb][k & 1], 0, 0, 0);
     }
-    if constexpr (kHeadGroups == 2) {
-      // Two consumer waves per CU leave LDS bandwidth to spare, but under
+    if constexpr (kHeadGroups >= 2) {
+      // One or two consumer waves per CU leave LDS bandwidth to spare, but under
       // register pressure the compiler issues each K read just before its
       // MFMA and waits out the LDS latency.  Pin the order: the prologue
       // reads, then per k-step the reads of step k + kQkAhead before the two
@@ -593,7 +594,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_gather_kernel(const GatherPar
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const int nblk = p.batch * p.nsplit * p.head_groups;
-  if (p.head_groups == 2)
+  if (p.head_groups == 4)
+    hipLaunchKernelGGL(mla_decode_kernel<4>, dim3(nblk), dim3(kThreads), 0, stream, p);
+  else if (p.head_groups == 2)
     hipLaunchKernelGGL(mla_decode_kernel<2>, dim3(nblk), dim3(kThreads), 0, stream, p);
   else
     hipLaunchKernelGGL(mla_decode_kernel<1>, dim3(nblk), dim3(kThreads), 0, stream, p);

@@ -66,7 +66,7 @@ def _decode(lib, q=0x1000, kv=0x1000, num_pages=1, pt=0x1000, max_pages=1, idx=0
     (dict(q=0x1008), -3), (dict(kv=0x1004), -3), (dict(out=0x1004), -3), (dict(lse=0x1002), -3),
     (dict(idx=0x1002), -3), (dict(scale=float("nan")), -4), (dict(scale=float("inf")), -4),
     (dict(batch=0), 0), (dict(batch=0, q=0, out=0, lse=0), 0),
-    (dict(topk=600, nsplit=2), -2), (dict(nsplit=2, hg=3), -2), (dict(nsplit=0, hg=-1), -2),
+    (dict(topk=600, nsplit=2), -2), (dict(nsplit=2, hg=3), -2), (dict(nsplit=2, hg=5), -2), (dict(nsplit=0, hg=-1), -2),
 ])
 def test_host_validation_without_device(kw, code):
     lib = m.load_library()
@@ -115,17 +115,19 @@ def test_append_validation_without_device(kw, code):
 
 @pytest.mark.parametrize("batch,topk,req,cus,expect", [
     (64, 512, 0, 256, (2, 256, 2)),    # 4 workgroups per query: 2 slices x 2 head groups
-    (1, 512, 0, 256, (8, 64, 2)),      # small batch: slices of at least 64 entries
+    (1, 512, 0, 256, (8, 64, 4)),      # small batch: slices of at least 64 entries
     (16, 512, 0, 256, (8, 64, 2)),
+    (2, 512, 0, 256, (8, 64, 4)),      # B * nsplit * 4 <= CUs / 4: 16-head workgroups
+    (4, 512, 0, 256, (8, 64, 2)),
     (32, 512, 0, 256, (4, 128, 2)),
     (128, 512, 0, 256, (1, 512, 2)),   # 2 workgroups per query: head groups, no split
     (100, 512, 0, 256, (1, 512, 2)),
     (129, 512, 0, 256, (1, 512, 1)),   # batch fills the GPU: 64 heads, no split
     (256, 512, 0, 256, (1, 512, 1)),
-    (1, 64, 0, 256, (1, 64, 2)),
-    (3, 300, 0, 256, (5, 64, 2)),      # ragged top-k
-    (3, 45, 0, 256, (1, 64, 2)),
-    (1, 0, 0, 256, (1, 32, 2)),        # empty top-k: one slice, writes zeros / -inf
+    (1, 64, 0, 256, (1, 64, 4)),
+    (3, 300, 0, 256, (5, 64, 4)),      # ragged top-k
+    (3, 45, 0, 256, (1, 64, 4)),
+    (1, 0, 0, 256, (1, 32, 4)),        # empty top-k: one slice, writes zeros / -inf
     (64, 512, 1, 256, (1, 512, 2)),    # forced
     (64, 512, 3, 256, (3, 192, 1)),    # slices hold whole 32-token tiles
     (64, 512, 99, 256, (16, 32, 1)),   # clamped to ceil(topk/32)

@@ -132,16 +132,17 @@ def test_decode_forced_split(i, nsplit):
 
 @pytest.mark.parametrize("i,nsplit", [(0, 1), (1, 1), (1, 8), (2, 4), (2, 8), (3, 2), (3, 1)])
 def test_head_groups_bitwise_equal(i, nsplit):
-    """Two 32-head workgroups per slice compute exactly what one 64-head
-    workgroup computes: the same tiles in the same order with the same
-    instructions per head, so the results agree bit for bit."""
+    """Two 32-head or four 16-head workgroups per slice compute exactly what
+    one 64-head workgroup computes: the same tiles in the same order with the
+    same instructions per head, so the results agree bit for bit."""
     w, (ref_out, ref_lse) = config(i)
     print(f"head groups config {i} nsplit={nsplit}", flush=True)
     d = to_device(w)
     r = [mlasd.mla_sparse_decode(d["q"], d["kv_pages"], d["page_table"], d["topk_idx"], d["seq_lens"],
-                                 w.softmax_scale, nsplit=nsplit, head_groups=hg) for hg in (1, 2)]
+                                 w.softmax_scale, nsplit=nsplit, head_groups=hg) for hg in (1, 2, 4)]
     torch.cuda.synchronize()
-    assert torch.equal(r[0][0], r[1][0]) and torch.equal(r[0][1], r[1][1])
+    for o, l in r[1:]:
+        assert torch.equal(r[0][0], o) and torch.equal(r[0][1], l)
     check_attention(r[1][0], r[1][1], ref_out, ref_lse, label=f"config {i} nsplit={nsplit} 32-head groups")
 
 
@@ -388,7 +389,7 @@ def test_validation_matrix(batch, topk):
     ref_out, ref_lse = O.sparse_mla_decode(w.q_bits, w.kv_pages, w.page_table, w.topk_idx,
                                            w.seq_lens, w.softmax_scale)
     d = to_device(w)
-    for ns, hg in ((None, None), (1, 1), (1, 2)):
+    for ns, hg in ((None, None), (1, 1), (1, 2), (1, 4)):
         out, lse = mlasd.mla_sparse_decode(d["q"], d["kv_pages"], d["page_table"], d["topk_idx"],
                                            d["seq_lens"], w.softmax_scale, nsplit=ns, head_groups=hg)
         torch.cuda.synchronize()
