@@ -376,6 +376,22 @@ def test_split_merge_alternating_inputs():
     check_attention(o, l, ref_s[0], ref_s[1], label="smaller batch after")
 
 
+def test_large_batch_several_rounds():
+    """B = 1000 queries: four rounds of workgroups on 256 CUs, 64-head
+    workgroups and no split; ragged lengths (some shorter than topk, so their
+    lists end in -1 padding)."""
+    rng = np.random.default_rng(1000)
+    lens = rng.integers(20, 700, 1000)
+    w = G.build_workload(5150, lens, 100, name="B=1000 topk=100")
+    ns, _, hg = mlasd.plan(w.batch, w.topk)
+    assert (ns, hg) == (1, 1)
+    print(f"large batch: plan nsplit={ns} head_groups={hg}", flush=True)
+    ref_out, ref_lse = O.sparse_mla_decode(w.q_bits, w.kv_pages, w.page_table, w.topk_idx,
+                                           w.seq_lens, w.softmax_scale)
+    out, lse = run(w)
+    check_attention(out, lse, ref_out, ref_lse, label="B=1000 topk=100")
+
+
 # ----------------------------------------------------------------------------
 # the pages' validation matrix ("The Moment of Validation", "The Third
 # Attempt"): B in {1, 4, 16, 32}, 64 heads, topk in {128, 512}
