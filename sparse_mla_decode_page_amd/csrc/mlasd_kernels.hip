@@ -10,10 +10,12 @@
 // a whole number of 32-wide MFMA K-steps, so the pages' pad-to-512 mask has
 // nothing to do on this hardware.
 //
-// Workgroup = (query b, slice s of its top-k list), 512 threads = 8 waves in
-// two roles, one wave of each role per SIMD, meeting at one barrier per
-// 32-token tile:
-//   consumers (waves 0..3): wave c owns heads [16c, 16c+16) and runs
+// Workgroup = (query b, slice s of its top-k list, head group), 512 threads =
+// 8 waves in two roles, one wave of each role per SIMD, meeting at one
+// barrier per 32-token tile:
+//   consumers (waves 0..3): wave c owns heads [16c, 16c+16) of the
+//       workgroup's head group (64, 32 or 16 heads; with fewer than 64, the
+//       spare consumer waves only pass the barriers) and runs
 //       a4  S^T = K Q^T on v_mfma_f32_16x16x32_bf16, Q held in registers;
 //       a5  online softmax in fp32 (exp2 domain), one head per lane column;
 //       a6  O^T += V^T P^T on v_mfma_f32_16x16x32_f16 over all 448 dims, the
@@ -21,8 +23,8 @@
 //       a7  epilogue: bf16 out + fp32 lse, or fp32 partials for the combine;
 //   producers (waves 4..7): wave p owns tokens [8p, 8p+8) of every tile and
 //       a2  gathers their records (576 B + 8 B scale record) into registers
-//           four tiles ahead, with loads whose issue never depends on data
-//           (masked slots re-read the slice's last valid record);
+//           kDepth + 1 tiles ahead, with loads whose issue never depends on
+//           data (masked slots re-read the slice's last valid record);
 //       a3  dequantises tile t+1 into the other LDS buffer (K bf16 token-major,
 //           V fp16 token-major with rows in PV k-slot order) while the
 //           consumers work on tile t.
