@@ -56,27 +56,38 @@ def workload_stats(w):
 
 
 def cpu_baseline(w, seconds):
-    """Time the fp64 CPU oracle on passes over the same workload (set 0)."""
+    """Time the fp64 CPU oracle on passes over the same workload (set 0), with
+    every BLAS thread, then (for a fifth of the time) with one thread."""
     from oracle.mla_oracle import sparse_mla_decode as oracle_decode
+    st = workload_stats(w)
+
+    def rate(budget):
+        passes, t0 = 0, time.perf_counter()
+        while True:
+            oracle_decode(w.q_bits, w.kv_pages, w.page_table, w.topk_idx, w.seq_lens, w.softmax_scale)
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= budget or passes >= 1000:
+                return st["attended"] * passes / el, passes, el
+
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
                       or [1])
     except Exception:  # threadpoolctl missing: report the process's CPU affinity
+        threadpool_limits = None
         threads = len(os.sched_getaffinity(0))
-    st = workload_stats(w)
-    passes, t0 = 0, time.perf_counter()
-    while True:
-        oracle_decode(w.q_bits, w.kv_pages, w.page_table, w.topk_idx, w.seq_lens, w.softmax_scale)
-        passes += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or passes >= 1000:
-            break
-    return {"value": st["attended"] * passes / el, "unit": "attended (query*head*token)/s",
+    value, passes, el = rate(seconds)
+    one = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1, user_api="blas"):
+            one = rate(max(1.0, seconds / 5))[0]
+    return {"value": value, "unit": "attended (query*head*token)/s",
             "cores": int(threads), "kind": "oracle",
+            "value_1_thread": one,
             "sample": f"{passes} full pass(es) of the timed workload's first input set "
                       f"({w.batch} queries, {st['n_valid']} valid entries) in {el:.1f} s; "
-                      f"numpy float64 with {threads} BLAS thread(s)"}
+                      f"numpy float64 with {threads} BLAS thread(s), then 1 thread"}
 
 
 def copy_bandwidth(dev, mib=1024, reps=5):
