@@ -213,3 +213,31 @@ def test_append_large_sampled():
         assert np.array_equal(got[page, slot * 576:(slot + 1) * 576], rec), f"token {t}"
         assert np.array_equal(got[page, O.SCALE_REGION + 8 * slot:O.SCALE_REGION + 8 * slot + 8], sc), \
             f"token {t} scales"
+
+
+def test_append_graph_capture_replay():
+    """The append captured in a HIP graph replays to the oracle's bytes: three
+    replays, with the pool restored by eager work between them."""
+    rng = np.random.default_rng(77)
+    page_table = np.array([[2, 0], [1, -1]], dtype=np.int32)
+    seq = np.array([0] * 30 + [1] * 30, np.int32)
+    pos = np.concatenate([rng.choice(512, 30, replace=False), rng.choice(256, 30, replace=False)]).astype(np.int32)
+    bits = _group_mix(60, 78)
+    pool = _pool(3, 79)
+    ref = O.kv_append(pool, page_table, seq, pos, bits)
+    dev = torch.device("cuda")
+    kv = torch.from_numpy(pool).to(dev)
+    pool_dev = kv.clone()
+    lat = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    ids, ps, pt = (torch.from_numpy(v).to(dev) for v in (seq, pos, page_table))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        mlasd.mla_kv_append(lat, ids, ps, pt, kv, stream=s)
+    for rep in range(3):
+        kv.copy_(pool_dev)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _assert_pool_equal(kv.cpu().numpy(), ref, f"graph replay {rep}")
