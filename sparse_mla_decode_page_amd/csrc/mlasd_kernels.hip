@@ -48,7 +48,8 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = kThreads / 64;
 constexpr int kConsumers = 4;       // waves 0..3
-constexpr int kKRow = kDQK + 8;     // K tile row stride (bf16 elements), +16 B pad
+constexpr int kKRow = kDQK + 16;    // K tile row stride (bf16 elements), +32 B pad: of the
+                                    // pads tried (16-64 B) the fastest with 64 heads
 constexpr int kVRow = kDQK + 16;    // V tile row stride (fp16 elements): 448 dims, a
                                     // 64-element spill area for lanes 56..63, +32 B pad
 constexpr int kDepth = 2;           // tiles gathered ahead by the producers
@@ -60,7 +61,7 @@ constexpr int kStageRowBytes = 912; // epilogue staging row: 896 B (+16 B pad)
 constexpr int kStageBytes = 16 * kStageRowBytes;   // one wave's 16 rows
 
 struct __align__(16) Smem {
-  uint16_t k[2][kTileTokens * kKRow];   // 2 x 33,280 B
+  uint16_t k[2][kTileTokens * kKRow];   // 2 x 33,792 B
   uint16_t v[2][kTileTokens * kVRow];   // 2 x 33,792 B
   int32_t tok[kMaxTopk][2];             // compacted list: physical page, slot
   uint16_t tok_entry[kMaxTopk];         //                 entry index in the slice
