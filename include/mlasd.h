@@ -94,6 +94,13 @@ enum {
  *   stream     HIP stream to enqueue on.
  *
  * batch == 0 is a no-op.  topk == 0 writes out = 0, lse = -inf.
+ * Numerics: the 448 nope dims of q and K, and the value rows, enter the
+ * contractions in fp16; the 64 rope dims in bf16; sums and the softmax are
+ * fp32.  Dequantised cache values are exact in fp16 while their magnitude is
+ * below 65520 and they are multiples of 2^-24 (UE8M0 exponents -15..7 for
+ * e4m3 bytes); q's nope values are exact in fp16 for magnitudes in
+ * [2^-14, 65504] and keep every bit down to 2^-24 below that.  Larger values
+ * overflow to infinity.
  * Returns MLASD_OK or a negative MLASD_ERR_* code.
  */
 int mla_sparse_decode(const void* q,
@@ -146,9 +153,10 @@ int mla_sparse_plan(int32_t batch, int32_t topk, int32_t nsplit_request, int32_t
  * runs the same index resolution, page-table walk, gather and dequantisation
  * code as the decode kernel and writes what the contractions consume.
  *
- *   k_rows  bf16 [batch, topk, 512]: dequantised key row of each entry (the
- *           QK^T operand; nope e4m3 * 2^(e-127) and rope, both exact in bf16
- *           when the value is representable).  Zero for masked entries.
+ *   k_rows  bf16 [batch, topk, 512]: key row of each entry as the QK^T
+ *           contraction consumes it: nope e4m3 * 2^(e-127) rounded to fp16
+ *           (as in v_rows) and written widened to bf16, which is exact;
+ *           rope as stored.  Zero for masked entries.
  *   v_rows  fp16 [batch, topk, 448]: the value row of each entry as the PV
  *           contraction consumes it (fp16; exact while every dequantised
  *           value is a multiple of 2^-24 of magnitude <= 65504).  Zero for

@@ -16,7 +16,9 @@
 //   consumers (waves 0..3): wave c owns heads [16c, 16c+16) of the
 //       workgroup's head group (64, 32 or 16 heads; with fewer than 64, the
 //       spare consumer waves only pass the barriers) and runs
-//       a4  S^T = K Q^T on v_mfma_f32_16x16x32_bf16, Q held in registers;
+//       a4  S^T = K Q^T, Q held in registers: the 448 nope dims on
+//           v_mfma_f32_16x16x32_f16 (K and Q in fp16), the 64 rope dims on
+//           v_mfma_f32_16x16x32_bf16;
 //       a5  online softmax in fp32 (exp2 domain), one head per lane column;
 //       a6  O^T += V^T P^T on v_mfma_f32_16x16x32_f16 over all 448 dims, the
 //           V^T operand read with ds_read_b64_tr_b16 transposing loads;
@@ -25,9 +27,11 @@
 //       a2  gathers their records (576 B + 8 B scale record) into registers
 //           kDepth + 1 tiles ahead, with loads whose issue never depends on
 //           data (masked slots re-read the slice's last valid record);
-//       a3  dequantises tile t+1 into the other LDS buffer (K bf16 token-major,
-//           V fp16 token-major with rows in PV k-slot order) while the
-//           consumers work on tile t.
+//       a3  dequantises tile t+1 into the other LDS buffer while the
+//           consumers work on tile t.  One token-major tile serves both
+//           contractions: a row holds the token's 448 nope values in fp16 (the
+//           K operand of the nope dims and the V operand) and its 64 rope
+//           values in bf16, so every nope byte is converted and stored once.
 //   a1  before that, all waves validate, resolve through the page table and
 //       compact the slice's entries into an LDS list;
 //   a8  the combine kernel merges slices with the LSE rule.
@@ -48,10 +52,10 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = kThreads / 64;
 constexpr int kConsumers = 4;       // waves 0..3
-constexpr int kKRow = kDQK + 16;    // K tile row stride (bf16 elements), +32 B pad: of the
-                                    // pads tried (16-64 B) the fastest with 64 heads
-constexpr int kVRow = kDQK + 16;    // V tile row stride (fp16 elements): 448 dims, a
-                                    // 64-element spill area for lanes 56..63, +32 B pad
+constexpr int kRow = kDQK + 16;     // tile row stride (16-bit elements): 448 fp16 nope,
+                                    // 64 bf16 rope, +32 B pad (of the pads tried, 16-64 B,
+                                    // the fastest with 64 heads)
+constexpr int kNopeSteps = kDNope / 32;   // 14 fp16 QK^T k-steps; 2 bf16 rope k-steps follow
 constexpr int kDepth = 2;           // tiles gathered ahead by the producers
 constexpr int kTokPerProducer = kTileTokens / (kWaves - kConsumers);   // 8
 constexpr float kRescaleLog2 = 8.f; // lazy-rescale threshold (P <= 256)
@@ -61,14 +65,12 @@ constexpr int kStageRowBytes = 912; // epilogue staging row: 896 B (+16 B pad)
 constexpr int kStageBytes = 16 * kStageRowBytes;   // one wave's 16 rows
 
 struct __align__(16) Smem {
-  uint16_t k[2][kTileTokens * kKRow];   // 2 x 33,792 B
-  uint16_t v[2][kTileTokens * kVRow];   // 2 x 33,792 B
+  uint16_t kv[2][kTileTokens * kRow];   // 2 x 33,792 B
   int32_t tok[kMaxTopk][2];             // compacted list: physical page, slot
   uint16_t tok_entry[kMaxTopk];         //                 entry index in the slice
   int32_t wave_cnt[kWaves];
 };
-static_assert(2 * kStageBytes <= (int)sizeof(Smem::k[0]) && 2 * kStageBytes <= (int)sizeof(Smem::v[0]),
-              "epilogue staging must fit one K and one V buffer");
+static_assert(kConsumers * kStageBytes <= (int)sizeof(Smem::kv), "epilogue staging must fit the tiles");
 
 // ---------------------------------------------------------------------------
 // small helpers
@@ -160,11 +162,6 @@ __device__ int compact_slice(Smem& sm, const int32_t* idx_row, int n_ent, int se
   return total;
 }
 
-// PV k-slot of tile token t.  A consumer's S^T accumulator block mb holds
-// tokens 16mb + 4g + r in lane group g, row r; they feed k-slots 8g + 4mb + r
-// of the P^T operand, so the V tile stores token t in row slot_of(t).
-__device__ __forceinline__ int slot_of(int t) { return 8 * ((t >> 2) & 3) + 4 * (t >> 4) + (t & 3); }
-
 // a2 registers of one tile for one producer wave p: tokens 8p + j, j = 0..7.
 //   rec[j]: lanes 0..55 hold nope bytes [8 lane, 8 lane + 8) of token j,
 //           lanes 56..63 hold token j's 8-byte scale record;
@@ -215,14 +212,14 @@ __device__ __forceinline__ void load_tile(TileRegs& r, const Smem& sm, const uin
 }
 
 // a3: dequantise one producer wave's 8 gathered tokens into LDS buffer `buf`.
-// Every lane stores 16 bytes per row at 16 * lane: lanes 0..55 hold dims
-// [8 lane, 8 lane + 8); lanes 56..63 (the scale-record lanes) land in the K
-// row's rope span, rewritten just after by the rope store, and in the V row's
-// spill area, which PV never reads.
+// Every lane stores 16 bytes per row at 16 * lane: lanes 0..55 hold nope dims
+// [8 lane, 8 lane + 8) in fp16; lanes 56..63 (the scale-record lanes) land in
+// the row's rope span, which the rope store rewrites just after (LDS stores of
+// one wave complete in order).  A scaled e4m3 value is exact in fp16 while
+// its magnitude stays below 2^16 and it is a multiple of 2^-24.
 __device__ __forceinline__ void store_tile(Smem& sm, const TileRegs& r, int buf, int pw, int lane) {
   const int g = lane >> 3;  // scale group of nope dims [8 lane, 8 lane + 8)
-  uint16_t* kb = &sm.k[buf][8 * lane];
-  uint16_t* vb = &sm.v[buf][8 * lane];
+  uint16_t* rb = &sm.kv[buf][8 * lane];
 #pragma unroll
   for (int j = 0; j < kTokPerProducer; ++j) {
     const uint32_t lo = __builtin_amdgcn_readlane(r.rec[j].x, 56);
@@ -230,21 +227,15 @@ __device__ __forceinline__ void store_tile(Smem& sm, const TileRegs& r, int buf,
     const uint32_t sb = ((g < 4) ? (lo >> (8 * g)) : (hi >> (8 * (g - 4)))) & 0xffu;
     const float scale = __uint_as_float(sb << 23);   // 2^(sb-127) as an fp32 power of two
     const uint32_t b0 = r.rec[j].x, b1 = r.rec[j].y;
-    u32x4 kq, vq;
-    kq.x = pack2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b0, scale, false));
-    kq.y = pack2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b0, scale, true));
-    kq.z = pack2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b1, scale, false));
-    kq.w = pack2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b1, scale, true));
+    u32x4 vq;
     vq.x = pack2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b0, scale, false));
     vq.y = pack2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b0, scale, true));
     vq.z = pack2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b1, scale, false));
     vq.w = pack2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b1, scale, true));
-    const int t = kTokPerProducer * pw + j;
-    *(u32x4*)(kb + t * kKRow) = kq;
-    *(u32x4*)(vb + slot_of(t) * kVRow) = vq;
+    *(u32x4*)(rb + (kTokPerProducer * pw + j) * kRow) = vq;
   }
   const int tr = kTokPerProducer * pw + (lane >> 3);
-  *(u32x4*)&sm.k[buf][tr * kKRow + kDNope + 8 * (lane & 7)] = r.rope;
+  *(u32x4*)&sm.kv[buf][tr * kRow + kDNope + 8 * (lane & 7)] = r.rope;
 }
 
 // ---------------------------------------------------------------------------
@@ -316,12 +307,23 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
   const int head0 = kHeads / kHeadGroups * hg + 16 * wid;   // the wave's first head
   const int head = head0 + col;
 
-  // Q^T operand for the wave's 16 heads, kept in registers: dims [32k + 8g, +8).
-  bf16x8 qreg[16];
+  // Q^T operand for the wave's 16 heads, kept in registers: dims [32k + 8g, +8);
+  // the nope k-steps in fp16 (exact for bf16 values of magnitude in
+  // [2^-14, 65504]; smaller ones keep every bit down to 2^-24), the rope
+  // k-steps in bf16.
+  f16x8 qnope[kNopeSteps];
+  bf16x8 qrope[2];
   {
     const uint16_t* qrow = p.q + ((int64_t)b * kHeads + head) * kDQK + 8 * g;
+    bf16x8 qb[16];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) qreg[k] = *(const bf16x8*)(qrow + 32 * k);
+    for (int k = 0; k < 16; ++k) qb[k] = *(const bf16x8*)(qrow + 32 * k);
+#pragma unroll
+    for (int k = 0; k < kNopeSteps; ++k)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qnope[k][i] = (_Float16)(float)qb[k][i];
+    qrope[0] = qb[kNopeSteps];
+    qrope[1] = qb[kNopeSteps + 1];
   }
   f32x4 oacc[28];
 #pragma unroll
@@ -333,23 +335,30 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
     const int buf = t & 1;
     // a4: S^T[token][head] for the tile's 32 tokens: two 16-token blocks,
     // two accumulation chains each, operands read kQkAhead k-steps ahead.
-    const uint16_t* krow = &sm.k[buf][col * kKRow + 8 * g];
-    bf16x8 ka[kQkAhead + 1][2];
+    const uint16_t* krow = &sm.kv[buf][col * kRow + 8 * g];
+    u32x4 ka[kQkAhead + 1][2];   // raw operand bits: fp16 nope or bf16 rope
 #pragma unroll
     for (int k = 0; k < kQkAhead; ++k)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) ka[k][mb] = *(const bf16x8*)(krow + 16 * mb * kKRow + 32 * k);
+      for (int mb = 0; mb < 2; ++mb) ka[k][mb] = *(const u32x4*)(krow + 16 * mb * kRow + 32 * k);
     f32x4 sc[2][2] = {};
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       if (k + kQkAhead < 16) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
-          ka[(k + kQkAhead) % (kQkAhead + 1)][mb] = *(const bf16x8*)(krow + 16 * mb * kKRow + 32 * (k + kQkAhead));
+          ka[(k + kQkAhead) % (kQkAhead + 1)][mb] = *(const u32x4*)(krow + 16 * mb * kRow + 32 * (k + kQkAhead));
       }
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        sc[mb][k & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[k % (kQkAhead + 1)][mb], qreg[k], sc[mb][k & 1], 0, 0, 0);
+      for (int mb = 0; mb < 2; ++mb) {
+        const u32x4 a = ka[k % (kQkAhead + 1)][mb];
+        if (k < kNopeSteps)
+          sc[mb][k & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), qnope[k],
+                                                                 sc[mb][k & 1], 0, 0, 0);
+        else
+          sc[mb][k & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                                  qrope[k - kNopeSteps], sc[mb][k & 1], 0, 0, 0);
+      }
     }
     if constexpr (kHeadGroups >= 2) {
       // One or two consumer waves per CU leave LDS bandwidth to spare, but under
@@ -407,17 +416,19 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
     rsum = group_sum4(rsum);
     l_run += rsum;
 
-    // a6: O^T[dim][head] += V^T P^T over the tile's 32 k-slots; the V^T
-    // operand comes from the token-major V tile through transposing reads:
-    // lane (g, c) addresses row 8g + c/4 (+4), dims d0 + 4(c%4), and receives
-    // V[8g..8g+3 (+4)][d0 + c].  Operands are read kPvAhead blocks ahead.
-    const uint16_t* vbase = &sm.v[buf][(8 * g + (col >> 2)) * kVRow + 4 * (col & 3)];
+    // a6: O^T[dim][head] += V^T P^T over the tile's 32 tokens.  The P^T
+    // operand of lane group g holds, in k-slots 8g + 4mb + r, the lane's
+    // scores of tokens 16mb + 4g + r; the V^T operand comes from the
+    // token-major tile through transposing reads: lane (g, c) addresses row
+    // 4g + c/4 (+16), dims d0 + 4(c%4), and receives V[4g..4g+3 (+16)][d0 + c].
+    // Operands are read kPvAhead blocks ahead.
+    const uint16_t* vbase = &sm.kv[buf][(4 * g + (col >> 2)) * kRow + 4 * (col & 3)];
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
     i16x4 vlo[kPvAhead + 1], vhi[kPvAhead + 1];
 #pragma unroll
     for (int mb = 0; mb < kPvAhead; ++mb) {
       vlo[mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 16 * mb));
-      vhi[mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 4 * kVRow + 16 * mb));
+      vhi[mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 16 * kRow + 16 * mb));
     }
 #pragma unroll
     for (int mb = 0; mb < 28; ++mb) {
@@ -425,7 +436,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
       if (nx < 28) {
         vlo[nx % (kPvAhead + 1)] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 16 * nx));
         vhi[nx % (kPvAhead + 1)] =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 4 * kVRow + 16 * nx));
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 16 * kRow + 16 * nx));
       }
       const f16x4 lo = __builtin_bit_cast(f16x4, vlo[mb % (kPvAhead + 1)]);
       const f16x4 hi = __builtin_bit_cast(f16x4, vhi[mb % (kPvAhead + 1)]);
@@ -451,11 +462,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
   // The wave's 16 output rows are contiguous in memory.  They are staged
   // through LDS so each store writes 1 KB of whole cache lines instead of 16
   // scattered 32-byte pieces: the store rate is bound by write requests in
-  // flight per CU, and this cuts them four-fold.  The staging area is the LDS
-  // buffer the last tile did not use; every wave finished its reads of it
-  // before the last barrier, and the producers write no LDS after it.
-  const int eb = ntiles & 1;
-  uint8_t* stage = (uint8_t*)(wid < 2 ? &sm.k[eb][0] : &sm.v[eb][0]) + (wid & 1) * kStageBytes;
+  // flight per CU, and this cuts them four-fold.  The staging area is the
+  // tile buffers: every wave finished its reads of them before the last
+  // barrier, and the producers write no LDS after it.
+  uint8_t* stage = (uint8_t*)&sm.kv[0][0] + wid * kStageBytes;
   if (p.nsplit == 1) {
 #pragma unroll
     for (int mb = 0; mb < 28; ++mb) {
@@ -583,9 +593,19 @@ __global__ __launch_bounds__(kThreads, 1) void mla_gather_kernel(const GatherPar
       const int ci = t * kTileTokens + tt;
       if (ci >= n_valid) continue;
       const int64_t e = (int64_t)b * p.topk + e0 + sm.tok_entry[ci];
-      *(u32x4*)(p.k_rows + e * kDQK + 8 * lane) = *(const u32x4*)&sm.k[0][tt * kKRow + 8 * lane];
-      if (lane < 56)
-        *(u32x4*)(p.v_rows + e * kDV + 8 * lane) = *(const u32x4*)&sm.v[0][slot_of(tt) * kVRow + 8 * lane];
+      // the tile row as the contractions read it: fp16 nope (written out as V
+      // and, widened to bf16, as K) and bf16 rope
+      const u32x4 raw = *(const u32x4*)&sm.kv[0][tt * kRow + 8 * lane];
+      u32x4 kq = raw;
+      if (lane < 56) {
+        const f16x8 h = __builtin_bit_cast(f16x8, raw);
+        kq.x = bf16x2_rne((float)h[0], (float)h[1]);
+        kq.y = bf16x2_rne((float)h[2], (float)h[3]);
+        kq.z = bf16x2_rne((float)h[4], (float)h[5]);
+        kq.w = bf16x2_rne((float)h[6], (float)h[7]);
+        *(u32x4*)(p.v_rows + e * kDV + 8 * lane) = raw;
+      }
+      *(u32x4*)(p.k_rows + e * kDQK + 8 * lane) = kq;
     }
     __syncthreads();
   }

@@ -80,10 +80,12 @@ def _all_codes_pool():
 
 
 def test_gather_dequant_all_codes_all_scales():
-    """The K operand is the exact dequantised value rounded to nearest-even
-    bf16, the V operand the same value rounded to fp16 (overflow -> inf):
-    identical to the oracle wherever the value is representable, which holds
-    for every value the workloads produce."""
+    """The nope part of both operands (K of the nope dims, and V) is the exact
+    dequantised value rounded to nearest-even fp16 (overflow -> inf); K's rope
+    part is the stored bf16 value.  The hook writes K widened to bf16, which
+    is exact: a rounded e4m3 value keeps at most 4 significant bits.  Both
+    are identical to the oracle wherever the value is representable in fp16,
+    which holds for every value the workloads produce."""
     pool = _all_codes_pool()
     pt = np.array([[0, 1]], dtype=np.int32)
     idx = np.arange(510, dtype=np.int32)[None][:, ::-1].copy()
@@ -95,8 +97,8 @@ def test_gather_dequant_all_codes_all_scales():
     assert ok.all() and valid.cpu().numpy().all()
     with np.errstate(over="ignore"):
         r32 = torch.from_numpy(rows.astype(np.float32))
-    exp_k = r32.to(torch.bfloat16).double().numpy()
     exp_v = r32[..., :448].to(torch.float16).double().numpy()
+    exp_k = np.concatenate([exp_v, r32[..., 448:].to(torch.bfloat16).double().numpy()], axis=-1)
     kk = _bf16_to_f64(k)
     vv = v.float().cpu().double().numpy()
     for got, want in ((kk, exp_k), (vv, exp_v)):
