@@ -380,41 +380,48 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
     // a5: online softmax.  Lane holds tokens 16mb + 4g + r of head `head`.
     const int tile_valid = n_valid - t * kTileTokens;
     float x[2][4];
-    float tmax = -INFINITY;   // this tile's max per head
+    float lmax = -INFINITY;   // max over the lane's own 8 scores
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const bool ok = (16 * mb + 4 * g + r) < tile_valid;
         x[mb][r] = ok ? sacc[mb][r] * p.scale_log2 : -INFINITY;
-        tmax = fmaxf(tmax, x[mb][r]);
+        lmax = fmaxf(lmax, x[mb][r]);
       }
-    tmax = group_max4(tmax);
     // Lazy rescale: O and l keep a reference max m_run; they are rescaled only
     // when some head of the wave sees its max rise by more than kRescaleLog2,
     // so P = exp2(x - m_run) stays <= 2^kRescaleLog2 (exact in fp16 range).
     // The quotient O / l is the same for any reference, so this changes no
-    // result beyond rounding.
-    if (__ballot(tmax > m_run + kRescaleLog2) != 0) {   // wave-uniform
+    // result beyond rounding.  P is taken against the current reference
+    // while the (rare) need to move it is decided from each lane's own
+    // scores, so the common path has no cross-lane reduction before PV.
+    float e[2][4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) e[mb][r] = __builtin_amdgcn_exp2f(x[mb][r] - m_run);
+    if (__ballot(lmax > m_run + kRescaleLog2) != 0) {   // wave-uniform
+      const float tmax = group_max4(lmax);              // the head's max over the tile
       const float m_new = fmaxf(m_run, tmax);          // finite: the tile has a valid token
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < 28; ++i) oacc[i] *= alpha;
       m_run = m_new;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) e[mb][r] = __builtin_amdgcn_exp2f(x[mb][r] - m_run);
     }
-    float rsum = 0.f;
     f16x8 pb;   // P^T operand, k-slot 8g + 4mb + r
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float e = __builtin_amdgcn_exp2f(x[mb][r] - m_run);
-        rsum += e;
-        pb[4 * mb + r] = (_Float16)e;
+        l_run += e[mb][r];   // the lane's share of l; lane groups are summed at the end
+        pb[4 * mb + r] = (_Float16)e[mb][r];
       }
-    rsum = group_sum4(rsum);
-    l_run += rsum;
 
     // a6: O^T[dim][head] += V^T P^T over the tile's 32 tokens.  The P^T
     // operand of lane group g holds, in k-slots 8g + 4mb + r, the lane's
@@ -456,6 +463,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
   }
 
   // a7: epilogue.  Lane holds O^T[16mb + 4g + r][head].
+  l_run = group_sum4(l_run);
   const bool empty = !(l_run > 0.f);
   const float inv = empty ? 0.f : 1.f / l_run;
   const float lse_v = empty ? -INFINITY : (m_run + __builtin_amdgcn_logf(l_run)) * 0.69314718055994531f;
