@@ -90,9 +90,15 @@ int stream_workspace(hipStream_t stream, size_t bytes, void** out) {
 //     instead of four and loads half of Q, and its sibling shares the
 //     gathered records through L2 (measured: c1 12.8 -> 11.2 us, c2 15.6 ->
 //     13.9 us, c3 with 2 slices of 32-head groups 23.8 us against 24.9 us
-//     with 4 slices of 64 heads); when most CUs would still idle (B <= 2 at
-//     topk 512), four head groups of 16 heads (c0 6.95 -> 6.3 us, c1 10.6 ->
-//     10.1 us);
+//     with 4 slices of 64 heads);
+//   - four head groups of 16 heads instead when a query gets at least 16
+//     workgroups (batch <= cus / 16), and for forced slice counts when
+//     batch * nsplit * 4 still leaves three quarters of the CUs idle: fewer
+//     slices then means fewer fp32 partials to write and merge (measured at
+//     topk 512: B=16 with (4 slices, 4 groups) 12.8 us against 13.2 us with
+//     (8, 2); B=4 10.6 against 11.1 us; but B=32 prefers (4, 2) 15.5 us over
+//     (2, 4) 17.0 us and B=48 (2, 2) 18.8 us over (1, 4) 20.0 us, where a
+//     16-head workgroup has too many tiles to walk alone);
 //   - the rest of the budget in top-k slices, none cut below kMinAutoSlice
 //     entries: every extra slice costs a partial write and read, and below
 //     two tiles a workgroup's fixed start-up cost (index resolution, first
@@ -105,11 +111,12 @@ void make_plan(int32_t batch, int32_t topk, int32_t ns_request, int32_t hg_reque
   const int tile = mlasd::kTileTokens;
   const int max_split = topk > 0 ? (topk + tile - 1) / tile : 1;
   const int per_query = batch > 0 ? cus / batch : cus;   // workgroups per query in one round
+  const bool four_groups = ns_request <= 0 && per_query >= 16;
   int ns;
   if (ns_request > 0) {
     ns = ns_request;
   } else {
-    ns = per_query >= 2 ? per_query / 2 : 1;
+    ns = four_groups ? per_query / 4 : per_query >= 2 ? per_query / 2 : 1;
     const int by_len = topk > 0 ? (topk + kMinAutoSlice - 1) / kMinAutoSlice : 1;
     if (ns > by_len) ns = by_len;
   }
@@ -122,8 +129,8 @@ void make_plan(int32_t batch, int32_t topk, int32_t ns_request, int32_t hg_reque
   *split_len = len;
   if (hg_request > 0)
     *head_groups = hg_request;
-  else if ((int64_t)batch * ns * 4 <= cus / 4)
-    *head_groups = 4;   // most CUs would idle: 16-head workgroups (B <= 2 at topk 512)
+  else if (four_groups || (int64_t)batch * ns * 4 <= cus / 4)
+    *head_groups = 4;
   else
     *head_groups = (int64_t)batch * ns * 2 <= cus ? 2 : 1;
 }

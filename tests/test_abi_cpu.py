@@ -116,9 +116,10 @@ def test_append_validation_without_device(kw, code):
 @pytest.mark.parametrize("batch,topk,req,cus,expect", [
     (64, 512, 0, 256, (2, 256, 2)),    # 4 workgroups per query: 2 slices x 2 head groups
     (1, 512, 0, 256, (8, 64, 4)),      # small batch: slices of at least 64 entries
-    (16, 512, 0, 256, (8, 64, 2)),
+    (16, 512, 0, 256, (4, 128, 4)),    # >= 16 workgroups per query: 16-head workgroups
     (2, 512, 0, 256, (8, 64, 4)),      # B * nsplit * 4 <= CUs / 4: 16-head workgroups
-    (4, 512, 0, 256, (8, 64, 2)),
+    (4, 512, 0, 256, (8, 64, 4)),
+    (17, 512, 0, 256, (6, 96, 2)),     # 15 workgroups per query: slices of 32-head groups
     (32, 512, 0, 256, (4, 128, 2)),
     (128, 512, 0, 256, (1, 512, 2)),   # 2 workgroups per query: head groups, no split
     (100, 512, 0, 256, (1, 512, 2)),
@@ -131,7 +132,7 @@ def test_append_validation_without_device(kw, code):
     (64, 512, 1, 256, (1, 512, 2)),    # forced
     (64, 512, 3, 256, (3, 192, 1)),    # slices hold whole 32-token tiles
     (64, 512, 99, 256, (16, 32, 1)),   # clamped to ceil(topk/32)
-    (8, 100, 0, 80, (2, 64, 2)),
+    (8, 100, 0, 80, (2, 64, 2)),       # 10 workgroups per query
     (32, 512, 0, 80, (1, 512, 2)),
 ])
 def test_plan(batch, topk, req, cus, expect):
