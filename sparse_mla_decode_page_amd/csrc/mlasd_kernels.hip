@@ -360,14 +360,12 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
                                                                   qrope[k - kNopeSteps], sc[mb][k & 1], 0, 0, 0);
       }
     }
-    if constexpr (kHeadGroups >= 2) {
-      // One or two consumer waves per CU leave LDS bandwidth to spare, but under
-      // register pressure the compiler issues each K read just before its
-      // MFMA and waits out the LDS latency.  Pin the order: the prologue
+    {
+      // Under register pressure the compiler issues each K read just before
+      // its MFMA and waits out the LDS latency.  Pin the order: the prologue
       // reads, then per k-step the reads of step k + kQkAhead before the two
-      // MFMAs of step k.  (With four consumer waves LDS bandwidth is the
-      // limit and this order is slower, so the 64-head kernel keeps the
-      // compiler's.)
+      // MFMAs of step k.  (Once K and V shared one tile, this order also
+      // became the faster one with four consumer waves: c4 27.8 -> 25.9 us.)
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * kQkAhead, 0);   // DS reads
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
