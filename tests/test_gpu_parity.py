@@ -239,6 +239,26 @@ def test_softmax_scale_values(scale):
     _check_custom(w, label=f"scale={scale}")
 
 
+@pytest.mark.parametrize("q_log2", [8, -6, "tiny"])
+def test_query_magnitudes(q_log2):
+    """Q's nope dims enter QK^T in fp16: exact for bf16 magnitudes in
+    [2^-14, 65504], every bit kept down to 2^-24 below that.  Q scaled by 2^8
+    (values up to ~1,200) or 2^-6, with the softmax scale compensating, and Q
+    with 5 % of its entries replaced by values near 1e-6 all meet the oracle
+    bar."""
+    w = _custom(21, [5000, 30000], 256)
+    q = (w.q_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if q_log2 == "tiny":
+        rng = np.random.default_rng(3)
+        pick = rng.random(q.shape) < 0.05
+        q = np.where(pick, rng.standard_normal(q.shape) * 1e-6, q)
+    else:
+        q = q * 2.0 ** q_log2
+        w.softmax_scale = w.softmax_scale * 2.0 ** -q_log2
+    w.q_bits = G.bf16_bits(q)
+    _check_custom(w, label=f"q scaled {q_log2}")
+
+
 def test_outliers_small_batch():
     w = _custom(13, [65536, 65536], 512, outlier_frac=0.01)
     for ns in (None, 1, 4):
