@@ -99,6 +99,11 @@ int stream_workspace(hipStream_t stream, size_t bytes, void** out) {
 //     (8, 2); B=4 10.6 against 11.1 us; but B=32 prefers (4, 2) 15.5 us over
 //     (2, 4) 17.0 us and B=48 (2, 2) 18.8 us over (1, 4) 20.0 us, where a
 //     16-head workgroup has too many tiles to walk alone);
+//   - four head groups and no split when they alone fill the GPU (4 * batch
+//     above 7/8 of the CUs, B = 57..64 on 256): the longer tile walk then costs
+//     less than the split's fp32 partials and combine launch (B=64, 65,536-
+//     token sequences: 20.4 us against 20.7-20.9 us for (2, 2), and 62.8 ->
+//     ~33 MB of HBM traffic per step; B=56: (2, 2) 19.5 us against 20.0 us);
 //   - the rest of the budget in top-k slices, none cut below kMinAutoSlice
 //     entries: every extra slice costs a partial write and read, and below
 //     two tiles a workgroup's fixed start-up cost (index resolution, first
@@ -111,12 +116,13 @@ void make_plan(int32_t batch, int32_t topk, int32_t ns_request, int32_t hg_reque
   const int tile = mlasd::kTileTokens;
   const int max_split = topk > 0 ? (topk + tile - 1) / tile : 1;
   const int per_query = batch > 0 ? cus / batch : cus;   // workgroups per query in one round
-  const bool four_groups = ns_request <= 0 && per_query >= 16;
+  const bool fill_by_groups = ns_request <= 0 && per_query == 4 && (int64_t)batch * 4 * 8 > (int64_t)cus * 7;
+  const bool four_groups = ns_request <= 0 && (per_query >= 16 || fill_by_groups);
   int ns;
   if (ns_request > 0) {
     ns = ns_request;
   } else {
-    ns = four_groups ? per_query / 4 : per_query >= 2 ? per_query / 2 : 1;
+    ns = four_groups ? per_query / 4 : per_query >= 2 ? per_query / 2 : 1;   // fill_by_groups: 1
     const int by_len = topk > 0 ? (topk + kMinAutoSlice - 1) / kMinAutoSlice : 1;
     if (ns > by_len) ns = by_len;
   }

@@ -114,7 +114,9 @@ def test_append_validation_without_device(kw, code):
 
 
 @pytest.mark.parametrize("batch,topk,req,cus,expect", [
-    (64, 512, 0, 256, (2, 256, 2)),    # 4 workgroups per query: 2 slices x 2 head groups
+    (64, 512, 0, 256, (1, 512, 4)),    # 4 workgroups per query filling the GPU: 4 head groups, no split
+    (56, 512, 0, 256, (2, 256, 2)),    # 4 workgroups per query, 224 of 256 CUs: 2 slices x 2 head groups
+    (64, 512, 0, 240, (1, 512, 2)),    # 3 workgroups per query: 2 head groups, no split
     (1, 512, 0, 256, (8, 64, 4)),      # small batch: slices of at least 64 entries
     (16, 512, 0, 256, (4, 128, 4)),    # >= 16 workgroups per query: 16-head workgroups
     (2, 512, 0, 256, (8, 64, 4)),      # B * nsplit * 4 <= CUs / 4: 16-head workgroups

@@ -328,7 +328,7 @@ def test_prepare_capture_release():
     """mlasd_prepare reserves a stream's split scratch, so a first split call
     made under graph capture allocates nothing; without it the growth is
     refused before anything is enqueued; mlasd_release frees the scratch."""
-    w, (ref_out, ref_lse) = config(3)   # B=64, topk=512: planned split
+    w, (ref_out, ref_lse) = config(2)   # B=16, topk=512: planned split (4 slices x 4 head groups)
     assert mlasd.plan(w.batch, w.topk)[0] > 1
     d = to_device(w)
     s = torch.cuda.Stream()
