@@ -65,7 +65,10 @@ constexpr int kStageRowBytes = 912; // epilogue staging row: 896 B (+16 B pad)
 constexpr int kStageBytes = 16 * kStageRowBytes;   // one wave's 16 rows
 
 struct __align__(16) Smem {
-  uint16_t kv[2][kTileTokens * kRow];   // 2 x 33,792 B
+  uint16_t kv[3][kTileTokens * kRow];   // 3 x 33,792 B (the 16-head kernel keeps three live)
+  u32x4 pex[2][64];                     // 16-head kernel: P^T operand handed to the PV helper wave
+  float aex[2][64];                     //                 and the rescale factor applied before it
+  float lx[64];                         //                 final l per lane column
   int32_t tok[kMaxTopk][2];             // compacted list: physical page, slot
   uint16_t tok_entry[kMaxTopk];         //                 entry index in the slice
   int32_t wave_cnt[kWaves];
@@ -238,6 +241,87 @@ __device__ __forceinline__ void store_tile(Smem& sm, const TileRegs& r, int buf,
   *(u32x4*)&sm.kv[buf][tr * kRow + kDNope + 8 * (lane & 7)] = r.rope;
 }
 
+// a6 over kBlocks 16-dim blocks: O^T[dim][head] += V^T P^T over the tile's 32
+// tokens.  The P^T operand of lane group g holds, in k-slots 8g + 4mb + r, the
+// lane's scores of tokens 16mb + 4g + r; the V^T operand comes from the
+// token-major tile through transposing reads: lane (g, c) addresses row
+// 4g + c/4 (+16), dims d0 + 4(c%4), and receives V[4g..4g+3 (+16)][d0 + c]
+// (vbase is the lane's address for the first block).  Operands are read
+// kPvAhead blocks ahead.
+template <int kBlocks>
+__device__ __forceinline__ void pv_blocks(f32x4* oacc, const uint16_t* vbase, f16x8 pb) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  i16x4 vlo[kPvAhead + 1], vhi[kPvAhead + 1];
+#pragma unroll
+  for (int mb = 0; mb < kPvAhead; ++mb) {
+    vlo[mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 16 * mb));
+    vhi[mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 16 * kRow + 16 * mb));
+  }
+#pragma unroll
+  for (int mb = 0; mb < kBlocks; ++mb) {
+    const int nx = mb + kPvAhead;
+    if (nx < kBlocks) {
+      vlo[nx % (kPvAhead + 1)] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 16 * nx));
+      vhi[nx % (kPvAhead + 1)] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 16 * kRow + 16 * nx));
+    }
+    const f16x4 lo = __builtin_bit_cast(f16x4, vlo[mb % (kPvAhead + 1)]);
+    const f16x4 hi = __builtin_bit_cast(f16x4, vhi[mb % (kPvAhead + 1)]);
+    const f16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    oacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb, oacc[mb], 0, 0, 0);
+  }
+  // V reads kPvAhead blocks ahead of their MFMAs (measured faster for 32
+  // heads, slightly faster for 64)
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPvAhead, 1);
+#pragma unroll
+  for (int mb = 0; mb < kBlocks; ++mb) {
+    if (mb + kPvAhead < kBlocks) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+  }
+}
+
+// a7 stores of one wave's 16 heads over dims [dim0, dim0 + 16 kBlocks):
+// bf16 out, or fp32 partials for the combine.  The wave's 16 output rows are
+// contiguous in memory.  They are staged through LDS (`stage`, the wave's own
+// area of the tile buffers, which every wave finished reading before the last
+// barrier and the producers no longer write) so each store writes whole 1 KB
+// runs of cache lines instead of 16 scattered 32-byte pieces: the store rate
+// is bound by write requests in flight per CU, and this cuts them four-fold.
+template <int kBlocks>
+__device__ __forceinline__ void store_out(const DecodeParams& p, uint8_t* stage, const f32x4* oacc, float inv,
+                                          int b, int s, int head0, int dim0, int lane) {
+  const int g = lane >> 4, col = lane & 15;
+  if (p.nsplit == 1) {
+#pragma unroll
+    for (int mb = 0; mb < kBlocks; ++mb) {
+      u32x2 w;
+      w.x = bf16x2_rne(oacc[mb][0] * inv, oacc[mb][1] * inv);
+      w.y = bf16x2_rne(oacc[mb][2] * inv, oacc[mb][3] * inv);
+      *(u32x2*)(stage + col * kStageRowBytes + 2 * (16 * mb + 4 * g)) = w;
+    }
+    uint8_t* obase = (uint8_t*)(p.out + ((int64_t)b * kHeads + head0) * kDV + dim0);
+    constexpr int kChunks = 2 * kBlocks;   // 16-byte chunks per row
+#pragma unroll
+    for (int k = 0; k < kBlocks / 2; ++k) {   // 16 rows x 32 kBlocks bytes
+      const int i = lane + 64 * k, row = i / kChunks, ch = i - kChunks * row;
+      *(u32x4*)(obase + row * (2 * kDV) + 16 * ch) = *(const u32x4*)(stage + row * kStageRowBytes + 16 * ch);
+    }
+  } else {
+    const int64_t prow0 = ((int64_t)b * p.nsplit + s) * kHeads + head0;
+#pragma unroll
+    for (int h = 0; h < kBlocks / 14; ++h) {   // fp32 partials, 224 dims per pass
+#pragma unroll
+      for (int mb = 0; mb < 14; ++mb)
+        *(f32x4*)(stage + col * kStageRowBytes + 4 * (16 * mb + 4 * g)) = oacc[14 * h + mb] * inv;
+#pragma unroll
+      for (int k = 0; k < 14; ++k) {   // 16 rows x 224 floats = 14 x 1 KB
+        const int i = lane + 64 * k, row = i / 56, ch = i - 56 * row;
+        *(f32x4*)(p.part_o + (prow0 + row) * kDV + dim0 + kDV / 2 * h + 4 * ch) =
+            *(const f32x4*)(stage + row * kStageRowBytes + 16 * ch);
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // a1-a7: main decode kernel
 // ---------------------------------------------------------------------------
@@ -262,8 +346,15 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
                                     p.max_pages, p.num_pages);
   const int ntiles = (n_valid + kTileTokens - 1) / kTileTokens;
 
+  // With 16-head workgroups a second consumer wave (the PV helper) runs PV
+  // over dims 224-447 one tile behind the main consumer wave, so three tile
+  // buffers are live and every role passes one more barrier at the end.
+  constexpr bool kHelper = kHeadGroups == 4;
+  constexpr int kBufs = kHelper ? 3 : 2;
+  constexpr int kExtra = kHelper ? 1 : 0;
+
   // Both roles pass the same barriers: one after the first tile is stored,
-  // then one per tile.
+  // then one per tile, then kExtra.
   if (wid >= kConsumers) {
     // ---------------- producers: a2 + a3 ----------------
     const int pw = wid - kConsumers;
@@ -284,7 +375,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
         for (int u = 0; u < kDepth; ++u) {
           const int t = t0 + u;
           const int nxt = (u + 1) % kDepth;   // ring slot of tile t + 1
-          if (t + 1 < ntiles) store_tile(sm, regs[nxt], (t + 1) & 1, pw, lane);
+          if (t + 1 < ntiles) store_tile(sm, regs[nxt], (t + 1) % kBufs, pw, lane);
           // issued on every path, so the loads in flight behind each ring slot
           // are the same wherever it is consumed (past the end they re-read a
           // cached record)
@@ -293,14 +384,46 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
         }
       }
     }
+    if (kExtra) __syncthreads();
     return;
   }
 
   // ---------------- consumers: a4 - a7 ----------------
   constexpr int kActive = kConsumers / kHeadGroups;   // consumer waves with heads
-  if (wid >= kActive) {   // spare consumer waves only pass the barriers
-    for (int t = 0; t <= ntiles; ++t) __syncthreads();
+  constexpr int kWork = kActive + (kHelper ? 1 : 0);   // ... and the PV helper
+  if (wid >= kWork) {   // spare consumer waves only pass the barriers
+    for (int t = 0; t <= ntiles + kExtra; ++t) __syncthreads();
     return;
+  }
+  if constexpr (kHelper) {
+    if (wid == 1) {
+      // PV helper: O^T over dims 224-447 of the main wave's 16 heads, for the
+      // tile before the one the main wave works on, with the P^T operand and
+      // rescale factor the main wave left in LDS.
+      const int g = lane >> 4, col = lane & 15;
+      f32x4 ohi[14];
+#pragma unroll
+      for (int i = 0; i < 14; ++i) ohi[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      __syncthreads();
+      for (int t = 0; t <= ntiles; ++t) {
+        if (t >= 1) {
+          const int pt = t - 1;
+          const f16x8 pb = __builtin_bit_cast(f16x8, sm.pex[pt & 1][lane]);
+          const float a = sm.aex[pt & 1][lane];
+          if (__ballot(a != 1.f) != 0) {
+#pragma unroll
+            for (int i = 0; i < 14; ++i) ohi[i] *= a;
+          }
+          pv_blocks<14>(ohi, &sm.kv[pt % kBufs][(4 * g + (col >> 2)) * kRow + 4 * (col & 3) + 16 * 14], pb);
+        }
+        __syncthreads();
+      }
+      const float l = sm.lx[lane];
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      const int head0 = kHeads / kHeadGroups * hg;
+      store_out<14>(p, (uint8_t*)&sm.kv[0][0] + wid * kStageBytes, ohi, inv, b, s, head0, kDV / 2, lane);
+      return;
+    }
   }
   const int g = lane >> 4;         // MFMA lane group
   const int col = lane & 15;       // MFMA column: head within the wave's 16
@@ -325,14 +448,15 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
     qrope[0] = qb[kNopeSteps];
     qrope[1] = qb[kNopeSteps + 1];
   }
-  f32x4 oacc[28];
+  constexpr int kOBlocks = kHelper ? 14 : 28;   // 16-dim blocks of O^T this wave keeps
+  f32x4 oacc[kOBlocks];
 #pragma unroll
-  for (int i = 0; i < 28; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < kOBlocks; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
+    const int buf = t % kBufs;
     // a4: S^T[token][head] for the tile's 32 tokens: two 16-token blocks,
     // two accumulation chains each, operands read kQkAhead k-steps ahead.
     const uint16_t* krow = &sm.kv[buf][col * kRow + 8 * g];
@@ -399,13 +523,14 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) e[mb][r] = __builtin_amdgcn_exp2f(x[mb][r] - m_run);
+    float alpha = 1.f;
     if (__ballot(lmax > m_run + kRescaleLog2) != 0) {   // wave-uniform
       const float tmax = group_max4(lmax);              // the head's max over the tile
       const float m_new = fmaxf(m_run, tmax);          // finite: the tile has a valid token
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
-      for (int i = 0; i < 28; ++i) oacc[i] *= alpha;
+      for (int i = 0; i < kOBlocks; ++i) oacc[i] *= alpha;
       m_run = m_new;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
@@ -420,6 +545,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
         l_run += e[mb][r];   // the lane's share of l; lane groups are summed at the end
         pb[4 * mb + r] = (_Float16)e[mb][r];
       }
+    if constexpr (kHelper) {   // for the helper, which runs PV over dims 224-447 next round
+      sm.pex[t & 1][lane] = __builtin_bit_cast(u32x4, pb);
+      sm.aex[t & 1][lane] = alpha;
+    }
 
     // a6: O^T[dim][head] += V^T P^T over the tile's 32 tokens.  The P^T
     // operand of lane group g holds, in k-slots 8g + 4mb + r, the lane's
@@ -427,81 +556,25 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
     // token-major tile through transposing reads: lane (g, c) addresses row
     // 4g + c/4 (+16), dims d0 + 4(c%4), and receives V[4g..4g+3 (+16)][d0 + c].
     // Operands are read kPvAhead blocks ahead.
-    const uint16_t* vbase = &sm.kv[buf][(4 * g + (col >> 2)) * kRow + 4 * (col & 3)];
-    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-    i16x4 vlo[kPvAhead + 1], vhi[kPvAhead + 1];
-#pragma unroll
-    for (int mb = 0; mb < kPvAhead; ++mb) {
-      vlo[mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 16 * mb));
-      vhi[mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 16 * kRow + 16 * mb));
-    }
-#pragma unroll
-    for (int mb = 0; mb < 28; ++mb) {
-      const int nx = mb + kPvAhead;
-      if (nx < 28) {
-        vlo[nx % (kPvAhead + 1)] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 16 * nx));
-        vhi[nx % (kPvAhead + 1)] =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 16 * kRow + 16 * nx));
-      }
-      const f16x4 lo = __builtin_bit_cast(f16x4, vlo[mb % (kPvAhead + 1)]);
-      const f16x4 hi = __builtin_bit_cast(f16x4, vhi[mb % (kPvAhead + 1)]);
-      const f16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      oacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb, oacc[mb], 0, 0, 0);
-    }
-    {   // V reads kPvAhead blocks ahead of their MFMAs (both kernels: measured
-        // faster for 32 heads, slightly faster for 64)
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPvAhead, 1);
-#pragma unroll
-      for (int mb = 0; mb < 28; ++mb) {
-        if (mb + kPvAhead < 28) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      }
-    }
+    pv_blocks<kOBlocks>(oacc, &sm.kv[buf][(4 * g + (col >> 2)) * kRow + 4 * (col & 3)], pb);
     __syncthreads();
   }
 
   // a7: epilogue.  Lane holds O^T[16mb + 4g + r][head].
   l_run = group_sum4(l_run);
+  if constexpr (kHelper) {   // the helper's last round: hand it l
+    sm.lx[lane] = l_run;
+    __syncthreads();
+  }
   const bool empty = !(l_run > 0.f);
   const float inv = empty ? 0.f : 1.f / l_run;
   const float lse_v = empty ? -INFINITY : (m_run + __builtin_amdgcn_logf(l_run)) * 0.69314718055994531f;
-  // The wave's 16 output rows are contiguous in memory.  They are staged
-  // through LDS so each store writes 1 KB of whole cache lines instead of 16
-  // scattered 32-byte pieces: the store rate is bound by write requests in
-  // flight per CU, and this cuts them four-fold.  The staging area is the
-  // tile buffers: every wave finished its reads of them before the last
-  // barrier, and the producers write no LDS after it.
-  uint8_t* stage = (uint8_t*)&sm.kv[0][0] + wid * kStageBytes;
-  if (p.nsplit == 1) {
-#pragma unroll
-    for (int mb = 0; mb < 28; ++mb) {
-      u32x2 w;
-      w.x = bf16x2_rne(oacc[mb][0] * inv, oacc[mb][1] * inv);
-      w.y = bf16x2_rne(oacc[mb][2] * inv, oacc[mb][3] * inv);
-      *(u32x2*)(stage + col * kStageRowBytes + 2 * (16 * mb + 4 * g)) = w;
-    }
-    uint8_t* obase = (uint8_t*)(p.out + ((int64_t)b * kHeads + head0) * kDV);
-#pragma unroll
-    for (int k = 0; k < 14; ++k) {   // 16 rows x 896 B = 14 x 1 KB
-      const int i = lane + 64 * k, row = i / 56, ch = i - 56 * row;
-      *(u32x4*)(obase + 16 * i) = *(const u32x4*)(stage + row * kStageRowBytes + 16 * ch);
-    }
-    if (g == 0) p.lse[(int64_t)b * kHeads + head] = lse_v;
-  } else {
-    const int64_t prow0 = ((int64_t)b * p.nsplit + s) * kHeads + head0;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {   // fp32 partials, 224 dims per pass
-#pragma unroll
-      for (int mb = 0; mb < 14; ++mb)
-        *(f32x4*)(stage + col * kStageRowBytes + 4 * (16 * mb + 4 * g)) = oacc[14 * h + mb] * inv;
-#pragma unroll
-      for (int k = 0; k < 14; ++k) {   // 16 rows x 224 floats = 14 x 1 KB
-        const int i = lane + 64 * k, row = i / 56, ch = i - 56 * row;
-        *(f32x4*)(p.part_o + (prow0 + row) * kDV + kDV / 2 * h + 4 * ch) =
-            *(const f32x4*)(stage + row * kStageRowBytes + 16 * ch);
-      }
-    }
-    if (g == 0) p.part_lse[((int64_t)b * p.nsplit + s) * kHeads + head] = lse_v;
+  store_out<kOBlocks>(p, (uint8_t*)&sm.kv[0][0] + wid * kStageBytes, oacc, inv, b, s, head0, 0, lane);
+  if (g == 0) {
+    if (p.nsplit == 1)
+      p.lse[(int64_t)b * kHeads + head] = lse_v;
+    else
+      p.part_lse[((int64_t)b * p.nsplit + s) * kHeads + head] = lse_v;
   }
 }
 
