@@ -221,20 +221,27 @@ __device__ __forceinline__ void load_tile(TileRegs& r, const Smem& sm, const uin
 // one wave complete in order).  A scaled e4m3 value is exact in fp16 while
 // its magnitude stays below 2^16 and it is a multiple of 2^-24.
 __device__ __forceinline__ void store_tile(Smem& sm, const TileRegs& r, int buf, int pw, int lane) {
-  const int g = lane >> 3;  // scale group of nope dims [8 lane, 8 lane + 8)
+  // The lane's scale is byte lane >> 3 of the token's 8-byte scale record,
+  // which lanes 56..63 hold: one v_perm_b32 picks it out of the two record
+  // words broadcast from lane 56.  All 8 scales are taken first, then the
+  // conversions and stores.
+  const uint32_t sel = 0x0C0C0C00u | (uint32_t)(lane >> 3);   // byte g, zero-extended
   uint16_t* rb = &sm.kv[buf][8 * lane];
+  float scale[kTokPerProducer];
 #pragma unroll
   for (int j = 0; j < kTokPerProducer; ++j) {
     const uint32_t lo = __builtin_amdgcn_readlane(r.rec[j].x, 56);
     const uint32_t hi = __builtin_amdgcn_readlane(r.rec[j].y, 56);
-    const uint32_t sb = ((g < 4) ? (lo >> (8 * g)) : (hi >> (8 * (g - 4)))) & 0xffu;
-    const float scale = __uint_as_float(sb << 23);   // 2^(sb-127) as an fp32 power of two
+    scale[j] = __uint_as_float(__builtin_amdgcn_perm(hi, lo, sel) << 23);   // 2^(sb-127) as an fp32 power of two
+  }
+#pragma unroll
+  for (int j = 0; j < kTokPerProducer; ++j) {
     const uint32_t b0 = r.rec[j].x, b1 = r.rec[j].y;
     u32x4 vq;
-    vq.x = pack2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b0, scale, false));
-    vq.y = pack2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b0, scale, true));
-    vq.z = pack2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b1, scale, false));
-    vq.w = pack2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b1, scale, true));
+    vq.x = pack2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b0, scale[j], false));
+    vq.y = pack2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b0, scale[j], true));
+    vq.z = pack2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b1, scale[j], false));
+    vq.w = pack2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b1, scale[j], true));
     *(u32x4*)(rb + (kTokPerProducer * pw + j) * kRow) = vq;
   }
   const int tr = kTokPerProducer * pw + (lane >> 3);
