@@ -14,8 +14,10 @@
 // 8 waves in two roles, one wave of each role per SIMD, meeting at one
 // barrier per 32-token tile:
 //   consumers (waves 0..3): wave c owns heads [16c, 16c+16) of the
-//       workgroup's head group (64, 32 or 16 heads; with fewer than 64, the
-//       spare consumer waves only pass the barriers) and runs
+//       workgroup's head group (64, 32 or 16 heads; with 32, waves 2..3 only
+//       pass the barriers; with 16, wave 1 is the PV helper, running a6 over
+//       dims 224-447 one tile behind wave 0, and waves 2..3 only pass the
+//       barriers) and runs
 //       a4  S^T = K Q^T, Q held in registers: the 448 nope dims on
 //           v_mfma_f32_16x16x32_f16 (K and Q in fp16), the 64 rope dims on
 //           v_mfma_f32_16x16x32_bf16;
