@@ -362,11 +362,17 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
   constexpr int kBufs = kHelper ? 3 : 2;
   constexpr int kExtra = kHelper ? 1 : 0;
 
+  // Roles by wave.  Waves w and w + 4 share a SIMD.  With 64 heads, waves
+  // 0..3 are consumers and 4..7 producers.  With fewer heads, the consumer
+  // waves that compute (0 and 1) get the spare waves (4 and 5) as SIMD
+  // partners, and the producers (2, 3, 6, 7) pair up on the other two SIMDs.
+  const bool producer = kHeadGroups == 1 ? wid >= kConsumers : (wid & 2) != 0;
+  const int pw = kHeadGroups == 1 ? wid - kConsumers : (wid & 1) + ((wid >> 2) << 1);   // producer index 0..3
+
   // Both roles pass the same barriers: one after the first tile is stored,
   // then one per tile, then kExtra.
-  if (wid >= kConsumers) {
+  if (producer) {
     // ---------------- producers: a2 + a3 ----------------
-    const int pw = wid - kConsumers;
     if (ntiles == 0) {   // empty slice: nothing to gather
       __syncthreads();
     } else {
@@ -400,7 +406,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
   // ---------------- consumers: a4 - a7 ----------------
   constexpr int kActive = kConsumers / kHeadGroups;   // consumer waves with heads
   constexpr int kWork = kActive + (kHelper ? 1 : 0);   // ... and the PV helper
-  if (wid >= kWork) {   // spare consumer waves only pass the barriers
+  if (wid >= kWork) {   // spare consumer waves (4, 5 with fewer than 64 heads) only pass the barriers
     for (int t = 0; t <= ntiles + kExtra; ++t) __syncthreads();
     return;
   }
