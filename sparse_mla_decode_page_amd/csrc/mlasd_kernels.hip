@@ -11,13 +11,14 @@
 // nothing to do on this hardware.
 //
 // Workgroup = (query b, slice s of its top-k list, head group), 512 threads =
-// 8 waves in two roles, one wave of each role per SIMD, meeting at one
-// barrier per 32-token tile:
-//   consumers (waves 0..3): wave c owns heads [16c, 16c+16) of the
-//       workgroup's head group (64, 32 or 16 heads; with 32, waves 2..3 only
-//       pass the barriers; with 16, wave 1 is the PV helper, running a6 over
-//       dims 224-447 one tile behind wave 0, and waves 2..3 only pass the
-//       barriers) and runs
+// 8 waves in two roles, meeting at one barrier per 32-token tile (waves w and
+// w + 4 share a SIMD):
+//   consumers: wave c owns heads [16c, 16c+16) of the workgroup's head group
+//       (64, 32 or 16 heads).  With 64 heads, waves 0..3, each beside a
+//       producer.  With 32, waves 0..1, each beside a spare wave (4, 5) that
+//       only passes the barriers.  With 16, wave 0, and wave 1 is the PV
+//       helper, running a6 over dims 224-447 one tile behind wave 0, again
+//       beside the spare waves.  A consumer runs
 //       a4  S^T = K Q^T, Q held in registers: the 448 nope dims on
 //           v_mfma_f32_16x16x32_f16 (K and Q in fp16), the 64 rope dims on
 //           v_mfma_f32_16x16x32_bf16;
@@ -25,7 +26,8 @@
 //       a6  O^T += V^T P^T on v_mfma_f32_16x16x32_f16 over all 448 dims, the
 //           V^T operand read with ds_read_b64_tr_b16 transposing loads;
 //       a7  epilogue: bf16 out + fp32 lse, or fp32 partials for the combine;
-//   producers (waves 4..7): wave p owns tokens [8p, 8p+8) of every tile and
+//   producers (waves 4..7 with 64 heads, else 2, 3, 6, 7, two per SIMD):
+//       producer p owns tokens [8p, 8p+8) of every tile and
 //       a2  gathers their records (576 B + 8 B scale record) into registers
 //           kDepth + 1 tiles ahead, with loads whose issue never depends on
 //           data (masked slots re-read the slice's last valid record);
