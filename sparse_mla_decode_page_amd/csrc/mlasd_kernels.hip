@@ -338,8 +338,9 @@ __device__ __forceinline__ void store_out(const DecodeParams& p, uint8_t* stage,
 // ---------------------------------------------------------------------------
 
 // kHeadGroups = 1: a workgroup computes all 64 heads of its (query, slice);
-// 2: 32 heads, with consumer waves 2..3 idle; 4: 16 heads, with consumer
-// waves 1..3 idle -- for batches too small to fill the GPU with slices alone.
+// 2: 32 heads on consumer waves 0..1; 4: 16 heads on consumer wave 0 with
+// wave 1 as its PV helper -- for batches too small to fill the GPU with
+// slices alone.  With 2 or 4, waves 4..5 are spare.
 // The head groups of a slice run on one XCD and share its gathered records
 // through L2.
 template <int kHeadGroups>
