@@ -16,9 +16,9 @@
 //   consumers: wave c owns heads [16c, 16c+16) of the workgroup's head group
 //       (64, 32 or 16 heads).  With 64 heads, waves 0..3, each beside a
 //       producer.  With 32, waves 0..1, each beside a spare wave (4, 5) that
-//       only passes the barriers.  With 16, wave 0, and wave 1 is the PV
-//       helper, running a6 over dims 224-447 one tile behind wave 0, again
-//       beside the spare waves.  A consumer runs
+//       only passes the barriers.  With 16, wave 0 runs a4 and a5 only, and
+//       two PV helpers (wave 1: dims 0-223, wave 4: dims 224-447) run a6 and
+//       a7 one tile behind it; wave 5 is spare.  A consumer runs
 //       a4  S^T = K Q^T, Q held in registers: the 448 nope dims on
 //           v_mfma_f32_16x16x32_f16 (K and Q in fp16), the 64 rope dims on
 //           v_mfma_f32_16x16x32_bf16;
@@ -65,7 +65,6 @@ constexpr int kTokPerProducer = kTileTokens / (kWaves - kConsumers);   // 8
 constexpr float kRescaleLog2 = 8.f; // lazy-rescale threshold (P <= 256)
 constexpr int kPvAhead = 3;         // PV operand blocks read ahead
 constexpr int kQkAhead = 3;         // QK^T operand k-steps read ahead
-constexpr int kSplitPvMaxTiles = 4; // 16-head slices up to this many tiles use the split-PV layout
 constexpr int kStageRowBytes = 912; // epilogue staging row: 896 B (+16 B pad)
 constexpr int kStageBytes = 16 * kStageRowBytes;   // one wave's 16 rows
 
@@ -339,18 +338,13 @@ __device__ __forceinline__ void store_out(const DecodeParams& p, uint8_t* stage,
 // ---------------------------------------------------------------------------
 
 // kHeadGroups = 1: a workgroup computes all 64 heads of its (query, slice);
-// 2: 32 heads on consumer waves 0..1; 4: 16 heads on consumer wave 0 with
-// wave 1 as its PV helper -- for batches too small to fill the GPU with
-// slices alone.  With 2 or 4, waves 4..5 are spare.  kSplitPv (16 heads,
-// slices of at most 4 tiles): the main wave keeps only Q K^T and the softmax,
-// and waves 1 and 5, which share a SIMD, are PV helpers for dims 0-223 and
-// 224-447; only wave 4 is spare.  Short slices gain from the shorter main
-// wave (c0 6.10 -> 5.92 us, c1 9.86 -> 9.76); a 16-tile slice loses 0.15 us.
-// The head groups of a slice run on one XCD and share its gathered records
-// through L2.
-template <int kHeadGroups, bool kSplitPv>
+// 2: 32 heads on consumer waves 0..1, waves 4..5 spare; 4: 16 heads, with
+// Q K^T and the softmax on wave 0 and P V on two helper waves (1: dims
+// 0-223, 4: dims 224-447), wave 5 spare -- for batches too small to fill the
+// GPU with slices alone.  The head groups of a slice run on one XCD and
+// share its gathered records through L2.
+template <int kHeadGroups>
 __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeParams p) {
-  static_assert(!kSplitPv || kHeadGroups == 4, "split PV needs 16-head workgroups");
   __shared__ Smem sm;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int blk = logical_block(p.batch * p.nsplit * kHeadGroups);
@@ -364,17 +358,19 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
                                     p.max_pages, p.num_pages);
   const int ntiles = (n_valid + kTileTokens - 1) / kTileTokens;
 
-  // With 16-head workgroups a second consumer wave (the PV helper) runs PV
-  // over dims 224-447 one tile behind the main consumer wave, so three tile
+  // With 16-head workgroups two PV helper waves run P V one tile behind the
+  // main consumer wave, which keeps only Q K^T and the softmax, so three tile
   // buffers are live and every role passes one more barrier at the end.
   constexpr bool kHelper = kHeadGroups == 4;
   constexpr int kBufs = kHelper ? 3 : 2;
   constexpr int kExtra = kHelper ? 1 : 0;
 
   // Roles by wave.  Waves w and w + 4 share a SIMD.  With 64 heads, waves
-  // 0..3 are consumers and 4..7 producers.  With fewer heads, the consumer
-  // waves that compute (0 and 1) get the spare waves (4 and 5) as SIMD
-  // partners, and the producers (2, 3, 6, 7) pair up on the other two SIMDs.
+  // 0..3 are consumers and 4..7 producers.  With fewer heads the producers
+  // are 2, 3, 6, 7 and pair up on two SIMDs.  With 32 heads the consumer
+  // waves 0 and 1 get the spare waves 4 and 5 as SIMD partners.  With 16,
+  // the main wave 0 shares its SIMD with PV helper 4 (dims 224-447) and PV
+  // helper 1 (dims 0-223) with spare wave 5.  Other layouts measured slower.
   const bool producer = kHeadGroups == 1 ? wid >= kConsumers : (wid & 2) != 0;
   const int pw = kHeadGroups == 1 ? wid - kConsumers : (wid & 1) + ((wid >> 2) << 1);   // producer index 0..3
 
@@ -414,17 +410,16 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
 
   // ---------------- consumers: a4 - a7 ----------------
   constexpr int kActive = kConsumers / kHeadGroups;   // consumer waves with heads
-  constexpr int kWork = kActive + (kHelper ? 1 : 0);   // ... and the PV helper
-  if (kSplitPv ? wid == 4 : wid >= kWork) {   // spare consumer waves (4, 5 with fewer than 64 heads) only pass the barriers
+  if (kHelper ? wid == 5 : wid >= kActive) {   // spare consumer waves only pass the barriers
     for (int t = 0; t <= ntiles + kExtra; ++t) __syncthreads();
     return;
   }
   if constexpr (kHelper) {
-    if (wid == 1 || (kSplitPv && wid == 5)) {
-      const int hb = kSplitPv && wid == 1 ? 0 : 14;   // first 16-dim block of the helper's dims
-      // PV helper: O^T over dims 224-447 of the main wave's 16 heads, for the
-      // tile before the one the main wave works on, with the P^T operand and
-      // rescale factor the main wave left in LDS.
+    if (wid == 1 || wid == 4) {
+      const int hb = wid == 1 ? 0 : 14;   // first 16-dim block of the helper's dims
+      // PV helper: O^T over its 224 dims of the main wave's 16 heads, for
+      // the tile before the one the main wave works on, with the P^T operand
+      // and rescale factor the main wave left in LDS.
       const int g = lane >> 4, col = lane & 15;
       f32x4 ohi[14];
 #pragma unroll
@@ -446,8 +441,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
       const float l = sm.lx[lane];
       const float inv = l > 0.f ? 1.f / l : 0.f;
       const int head0 = kHeads / kHeadGroups * hg;
-      store_out<14>(p, (uint8_t*)&sm.kv[0][0] + (kSplitPv ? 1 + hb / 14 : wid) * kStageBytes, ohi, inv, b, s, head0,
-                    16 * hb, lane);
+      store_out<14>(p, (uint8_t*)&sm.kv[0][0] + (1 + hb / 14) * kStageBytes, ohi, inv, b, s, head0, 16 * hb, lane);
       return;
     }
   }
@@ -474,7 +468,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
     qrope[0] = qb[kNopeSteps];
     qrope[1] = qb[kNopeSteps + 1];
   }
-  constexpr int kOBlocks = kHelper ? (kSplitPv ? 0 : 14) : 28;   // 16-dim blocks of O^T this wave keeps
+  constexpr int kOBlocks = kHelper ? 0 : 28;   // 16-dim blocks of O^T this wave keeps
   f32x4 oacc[kOBlocks > 0 ? kOBlocks : 1];
 #pragma unroll
   for (int i = 0; i < kOBlocks; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -571,7 +565,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
         l_run += e[mb][r];   // the lane's share of l; lane groups are summed at the end
         pb[4 * mb + r] = (_Float16)e[mb][r];
       }
-    if constexpr (kHelper) {   // for the helper, which runs PV over dims 224-447 next round
+    if constexpr (kHelper) {   // for the PV helpers, which run next round
       sm.pex[t & 1][lane] = __builtin_bit_cast(u32x4, pb);
       sm.aex[t & 1][lane] = alpha;
     }
@@ -588,7 +582,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
 
   // a7: epilogue.  Lane holds O^T[16mb + 4g + r][head].
   l_run = group_sum4(l_run);
-  if constexpr (kHelper) {   // the helper's last round: hand it l
+  if constexpr (kHelper) {   // the helpers' last round: hand them l
     sm.lx[lane] = l_run;
     __syncthreads();
   }
@@ -723,14 +717,12 @@ __global__ __launch_bounds__(kThreads, 1) void mla_gather_kernel(const GatherPar
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const int nblk = p.batch * p.nsplit * p.head_groups;
-  if (p.head_groups == 4 && p.split_len <= kSplitPvMaxTiles * kTileTokens)
-    hipLaunchKernelGGL((mla_decode_kernel<4, true>), dim3(nblk), dim3(kThreads), 0, stream, p);
-  else if (p.head_groups == 4)
-    hipLaunchKernelGGL((mla_decode_kernel<4, false>), dim3(nblk), dim3(kThreads), 0, stream, p);
+  if (p.head_groups == 4)
+    hipLaunchKernelGGL(mla_decode_kernel<4>, dim3(nblk), dim3(kThreads), 0, stream, p);
   else if (p.head_groups == 2)
-    hipLaunchKernelGGL((mla_decode_kernel<2, false>), dim3(nblk), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(mla_decode_kernel<2>, dim3(nblk), dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((mla_decode_kernel<1, false>), dim3(nblk), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(mla_decode_kernel<1>, dim3(nblk), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
