@@ -15,10 +15,10 @@
 // w + 4 share a SIMD):
 //   consumers: wave c owns heads [16c, 16c+16) of the workgroup's head group
 //       (64, 32 or 16 heads).  With 64 heads, waves 0..3, each beside a
-//       producer.  With 32, waves 0..1, each beside a spare wave (4, 5) that
-//       only passes the barriers.  With 16, wave 0 runs a4 and a5 only, and
-//       two PV helpers (wave 1: dims 0-223, wave 4: dims 224-447) run a6 and
-//       a7 one tile behind it; wave 5 is spare.  A consumer runs
+//       producer.  With 32, waves 0..1 run a4 and a5 only, each beside its
+//       PV helper (4, 5), which runs a6 and a7 one tile behind it.  With 16,
+//       wave 0 runs a4 and a5, and two PV helpers (wave 1: dims 0-223, wave
+//       4: dims 224-447) run a6 and a7; wave 5 is spare.  A consumer runs
 //       a4  S^T = K Q^T, Q held in registers: the 448 nope dims on
 //           v_mfma_f32_16x16x32_f16 (K and Q in fp16), the 64 rope dims on
 //           v_mfma_f32_16x16x32_bf16;
@@ -70,9 +70,9 @@ constexpr int kStageBytes = 16 * kStageRowBytes;   // one wave's 16 rows
 
 struct __align__(16) Smem {
   uint16_t kv[3][kTileTokens * kRow];   // 3 x 33,792 B (the 16-head kernel keeps three live)
-  u32x4 pex[2][64];                     // 16-head kernel: P^T operand handed to the PV helper wave
-  float aex[2][64];                     //                 and the rescale factor applied before it
-  float lx[64];                         //                 final l per lane column
+  u32x4 pex[2][2][64];                  // per consumer wave: P^T operand handed to its PV helpers
+  float aex[2][2][64];                  //                    and the rescale factor applied before it
+  float lx[2][64];                      //                    final l per lane column
   int32_t tok[kMaxTopk][2];             // compacted list: physical page, slot
   uint16_t tok_entry[kMaxTopk];         //                 entry index in the slice
   int32_t wave_cnt[kWaves];
@@ -338,10 +338,10 @@ __device__ __forceinline__ void store_out(const DecodeParams& p, uint8_t* stage,
 // ---------------------------------------------------------------------------
 
 // kHeadGroups = 1: a workgroup computes all 64 heads of its (query, slice);
-// 2: 32 heads on consumer waves 0..1, waves 4..5 spare; 4: 16 heads, with
-// Q K^T and the softmax on wave 0 and P V on two helper waves (1: dims
-// 0-223, 4: dims 224-447), wave 5 spare -- for batches too small to fill the
-// GPU with slices alone.  The head groups of a slice run on one XCD and
+// 2: 32 heads, Q K^T and the softmax on consumer waves 0..1 and P V on their
+// helpers 4..5; 4: 16 heads, Q K^T and the softmax on wave 0 and P V on two
+// helper waves (1: dims 0-223, 4: dims 224-447), wave 5 spare -- for
+// batches too small to fill the GPU with slices alone.  The head groups of a slice run on one XCD and
 // share its gathered records through L2.
 template <int kHeadGroups>
 __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeParams p) {
@@ -358,19 +358,20 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
                                     p.max_pages, p.num_pages);
   const int ntiles = (n_valid + kTileTokens - 1) / kTileTokens;
 
-  // With 16-head workgroups two PV helper waves run P V one tile behind the
-  // main consumer wave, which keeps only Q K^T and the softmax, so three tile
+  // With 16 or 32 heads, PV helper waves run P V one tile behind the
+  // consumer waves, which keep only Q K^T and the softmax, so three tile
   // buffers are live and every role passes one more barrier at the end.
-  constexpr bool kHelper = kHeadGroups == 4;
+  constexpr bool kHelper = kHeadGroups != 1;
   constexpr int kBufs = kHelper ? 3 : 2;
   constexpr int kExtra = kHelper ? 1 : 0;
 
   // Roles by wave.  Waves w and w + 4 share a SIMD.  With 64 heads, waves
   // 0..3 are consumers and 4..7 producers.  With fewer heads the producers
-  // are 2, 3, 6, 7 and pair up on two SIMDs.  With 32 heads the consumer
-  // waves 0 and 1 get the spare waves 4 and 5 as SIMD partners.  With 16,
-  // the main wave 0 shares its SIMD with PV helper 4 (dims 224-447) and PV
-  // helper 1 (dims 0-223) with spare wave 5.  Other layouts measured slower.
+  // are 2, 3, 6, 7 and pair up on two SIMDs.  With 32 heads, consumer waves
+  // 0 and 1 each share a SIMD with their PV helper (4 and 5).  With 16, the
+  // main wave 0 shares its SIMD with PV helper 4 (dims 224-447), and PV
+  // helper 1 (dims 0-223) its SIMD with spare wave 5.  Other layouts
+  // measured slower.
   const bool producer = kHeadGroups == 1 ? wid >= kConsumers : (wid & 2) != 0;
   const int pw = kHeadGroups == 1 ? wid - kConsumers : (wid & 1) + ((wid >> 2) << 1);   // producer index 0..3
 
@@ -409,39 +410,43 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
   }
 
   // ---------------- consumers: a4 - a7 ----------------
-  constexpr int kActive = kConsumers / kHeadGroups;   // consumer waves with heads
-  if (kHelper ? wid == 5 : wid >= kActive) {   // spare consumer waves only pass the barriers
+  if (kHeadGroups == 4 && wid == 5) {   // spare consumer waves only pass the barriers
     for (int t = 0; t <= ntiles + kExtra; ++t) __syncthreads();
     return;
   }
   if constexpr (kHelper) {
-    if (wid == 1 || wid == 4) {
-      const int hb = wid == 1 ? 0 : 14;   // first 16-dim block of the helper's dims
+    if (kHeadGroups == 4 ? (wid == 1 || wid == 4) : wid >= 4) {
+      // 16 heads: helpers 1 and 4 split consumer 0's dims; 32 heads: helper
+      // 4 + c runs all dims of consumer c.
+      constexpr int kHB = kHeadGroups == 4 ? 14 : 28;   // 16-dim blocks per helper
+      const int cw = kHeadGroups == 4 ? 0 : wid - 4;     // the consumer wave served
+      const int hb = kHeadGroups == 4 && wid == 4 ? 14 : 0;   // first 16-dim block
+      const int slot = kHeadGroups == 4 ? (wid == 1 ? 1 : 2) : 2 + cw;   // epilogue staging area
       // PV helper: O^T over its 224 dims of the main wave's 16 heads, for
       // the tile before the one the main wave works on, with the P^T operand
       // and rescale factor the main wave left in LDS.
       const int g = lane >> 4, col = lane & 15;
-      f32x4 ohi[14];
+      f32x4 ohi[kHB];
 #pragma unroll
-      for (int i = 0; i < 14; ++i) ohi[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < kHB; ++i) ohi[i] = f32x4{0.f, 0.f, 0.f, 0.f};
       __syncthreads();
       for (int t = 0; t <= ntiles; ++t) {
         if (t >= 1) {
           const int pt = t - 1;
-          const f16x8 pb = __builtin_bit_cast(f16x8, sm.pex[pt & 1][lane]);
-          const float a = sm.aex[pt & 1][lane];
+          const f16x8 pb = __builtin_bit_cast(f16x8, sm.pex[pt & 1][cw][lane]);
+          const float a = sm.aex[pt & 1][cw][lane];
           if (__ballot(a != 1.f) != 0) {
 #pragma unroll
-            for (int i = 0; i < 14; ++i) ohi[i] *= a;
+            for (int i = 0; i < kHB; ++i) ohi[i] *= a;
           }
-          pv_blocks<14>(ohi, &sm.kv[pt % kBufs][(4 * g + (col >> 2)) * kRow + 4 * (col & 3) + 16 * hb], pb);
+          pv_blocks<kHB>(ohi, &sm.kv[pt % kBufs][(4 * g + (col >> 2)) * kRow + 4 * (col & 3) + 16 * hb], pb);
         }
         __syncthreads();
       }
-      const float l = sm.lx[lane];
+      const float l = sm.lx[cw][lane];
       const float inv = l > 0.f ? 1.f / l : 0.f;
-      const int head0 = kHeads / kHeadGroups * hg;
-      store_out<14>(p, (uint8_t*)&sm.kv[0][0] + (1 + hb / 14) * kStageBytes, ohi, inv, b, s, head0, 16 * hb, lane);
+      const int head0 = kHeads / kHeadGroups * hg + 16 * cw;
+      store_out<kHB>(p, (uint8_t*)&sm.kv[0][0] + slot * kStageBytes, ohi, inv, b, s, head0, 16 * hb, lane);
       return;
     }
   }
@@ -566,8 +571,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
         pb[4 * mb + r] = (_Float16)e[mb][r];
       }
     if constexpr (kHelper) {   // for the PV helpers, which run next round
-      sm.pex[t & 1][lane] = __builtin_bit_cast(u32x4, pb);
-      sm.aex[t & 1][lane] = alpha;
+      sm.pex[t & 1][wid][lane] = __builtin_bit_cast(u32x4, pb);
+      sm.aex[t & 1][wid][lane] = alpha;
     }
 
     // a6: O^T[dim][head] += V^T P^T over the tile's 32 tokens.  The P^T
@@ -583,7 +588,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
   // a7: epilogue.  Lane holds O^T[16mb + 4g + r][head].
   l_run = group_sum4(l_run);
   if constexpr (kHelper) {   // the helpers' last round: hand them l
-    sm.lx[lane] = l_run;
+    sm.lx[wid][lane] = l_run;
     __syncthreads();
   }
   const bool empty = !(l_run > 0.f);
