@@ -167,6 +167,68 @@ def test_position_encoded_page_walk():
                 assert rows[b, j, 449] == p % 256
 
 
+def _page_id_pool(num_pages):
+    """Every record of page p has nope code 0x38 (1.0) at scale byte 127, so
+    nope dim 0 reads 1.0, and rope[0] = p, rope[1] = slot (exact in bf16): a
+    row names the record it came from."""
+    pool = np.zeros((num_pages, 256 * 584), dtype=np.uint8)
+    flat = pool.reshape(-1)
+    for p in range(num_pages):
+        for s in range(256):
+            base = p * 149504 + s * 576
+            flat[base:base + 448] = 0x38
+            for r, val in ((0, p), (1, s)):
+                bits = int(G.bf16_bits(np.array([float(val)]))[0])
+                flat[base + 448 + 2 * r] = bits & 0xFF
+                flat[base + 448 + 2 * r + 1] = bits >> 8
+        flat[p * 149504 + 147456:(p + 1) * 149504] = np.tile(np.array([127] * 7 + [0], np.uint8), 256)
+    return pool
+
+
+def test_masking_branches_by_hand():
+    """Reading R4 decided entry by entry (expected flags and rows written by
+    hand, not computed): a position below seq_len is still masked when its
+    page-table entry is -1, when its logical page lies past the page-table
+    row (seq_len larger than the row covers), or when the physical page id is
+    outside the pool.  A -1 page must not wrap round to the pool's last page,
+    and a logical page past the row must not index outside it."""
+    pool = _page_id_pool(3)
+    # max_pages = 3: the row covers positions 0..767; seq_len 1000 goes past it
+    pt = np.array([[2, -1, 0],
+                   [5, 1, 1]], dtype=np.int32)
+    lens = np.array([1000, 700], dtype=np.int32)
+    idx = np.array([[5, 300, 600, 800, 999, 767],
+                    [10, 256, 600, 700, -1, 699]], dtype=np.int32)
+    # (valid, page, slot) by hand:
+    #   q0: 5 -> lp 0 -> page 2 slot 5; 300 -> lp 1 -> page -1: masked;
+    #       600 -> lp 2 -> page 0 slot 88; 800 and 999 -> lp 3 >= max_pages: masked;
+    #       767 -> lp 2 -> page 0 slot 255
+    #   q1: 10 -> lp 0 -> page 5 >= num_pages 3: masked; 256 -> page 1 slot 0;
+    #       600 -> lp 2 -> page 1 slot 88; 700 = seq_len: masked; -1: masked;
+    #       699 -> page 1 slot 187
+    expect = [[(True, 2, 5), (False,), (True, 0, 88), (False,), (False,), (True, 0, 255)],
+              [(False,), (True, 1, 0), (True, 1, 88), (False,), (False,), (True, 1, 187)]]
+    valid, page, slot = O.resolve_entries(pt, idx, lens, 3)
+    rows, valid2 = O.gather_dequant(pool, pt, idx, lens)
+    assert np.array_equal(valid, valid2)
+    for b in range(2):
+        for j, e in enumerate(expect[b]):
+            assert bool(valid[b, j]) == e[0], (b, j)
+            if e[0]:
+                assert (page[b, j], slot[b, j]) == e[1:], (b, j)
+                assert rows[b, j, 0] == 1.0 and rows[b, j, 447] == 1.0
+                assert (rows[b, j, 448], rows[b, j, 449]) == e[1:], (b, j)
+            else:
+                assert np.all(rows[b, j] == 0), (b, j)
+    # the masked entries change nothing in the attention: query 0 over its
+    # three valid records equals query 0 over exactly those records
+    q = G.bf16_bits(np.random.default_rng(2).standard_normal((2, 64, 512)))
+    out, lse = O.sparse_mla_decode(q, pool, pt, idx, lens, 0.05)
+    out0, lse0 = O.sparse_mla_decode(q[:1], pool, pt[:1], idx[:1, [0, 2, 5]], lens[:1], 0.05)
+    np.testing.assert_array_equal(out[:1], out0)
+    np.testing.assert_array_equal(lse[:1], lse0)
+
+
 # ----------------------------------------------------------------------------
 # attention: against library routines and closed forms
 # ----------------------------------------------------------------------------
