@@ -23,27 +23,29 @@
  *                  (0 if no valid j)
  *
  * Cache layout ("The Validation Gate", "The Test Design: What Gets Validated
- * and How"): uint8 [num_pages, 149504].  Page p, slot s:
- *   token record at p*149504 + s*576: 448 e4m3 bytes, 64 little-endian bf16;
- *   scale record at p*149504 + 147456 + s*8: 7 UE8M0 bytes (byte g scales
- *   nope dims [64g, 64g+64)), then one ignored pad byte.
+ * and How"): a page is 149504 bytes.  Page p, slot s:
+ *   token record at s*576: 448 e4m3 bytes, then 64 little-endian bf16;
+ *   scale record at 147456 + s*8: 7 UE8M0 bytes (byte g scales nope dims
+ *   [64g, 64g+64)), then one ignored pad byte.
+ * Pages may sit at any row stride of at least 149504 bytes (a multiple of
+ * 16), e.g. a view of a wider pool -- the pages' own harness passes such a
+ * strided view ("The Validation Gate", "The Thinking Process").
  *
  * Conventions for every entry point:
- *   - All tensor pointers are DEVICE pointers owned by the caller, contiguous,
- *     row-major, in the dtype stated.  The library never frees them.
- *   - Every call is asynchronous on `stream` (0 = the null stream): it only
- *     enqueues work and never synchronises the host.
+ *   - Tensors are passed as mlasd_tensor descriptors: a DEVICE pointer owned
+ *     by the caller, a dtype, a shape and strides in elements.  Each entry
+ *     point states the dtype, shape and stride rules it accepts; the
+ *     innermost dimension is always contiguous (stride 1).  The library never
+ *     frees or keeps caller memory.
+ *   - Every call is asynchronous on `stream` (NULL = the null stream): it
+ *     only enqueues work.  No compute entry point allocates device memory or
+ *     synchronises the host; only mlasd_prepare / mlasd_reserve allocate and
+ *     only mlasd_release frees.
  *   - Arguments are validated on the host before anything is enqueued; on a
  *     non-zero return nothing was enqueued (except MLASD_ERR_HIP, which
  *     reports a failed enqueue).  Data-dependent conditions (masked indices,
  *     out-of-range page ids) are not errors: such entries are skipped.
- *   - Split scratch (fp32 partial outputs when a query's top-k list is cut
- *     into slices) is owned by the library: one buffer per (device, stream),
- *     grown with hipMalloc when a call needs more and kept until the process
- *     ends.  Calls on different streams may run concurrently; calls on one
- *     stream are ordered by the stream.  Growth synchronises the stream and
- *     is refused with MLASD_ERR_CAPTURE while the stream is capturing a
- *     graph: make a first call of the largest shape before capture.
+ *   - Output tensors must not overlap each other or any input.
  */
 #ifndef MLASD_H
 #define MLASD_H
@@ -59,14 +61,30 @@ typedef struct ihipStream_t* mlasd_stream_t; /* same object as hipStream_t */
 
 enum {
   MLASD_OK = 0,
-  MLASD_ERR_NULL = -1,      /* a required pointer is NULL                         */
-  MLASD_ERR_SHAPE = -2,     /* a size is out of range (batch<0, topk>512, ...)   */
-  MLASD_ERR_ALIGN = -3,     /* a pointer is not aligned as stated                 */
-  MLASD_ERR_VALUE = -4,     /* a scalar argument is invalid (non-finite scale)    */
+  MLASD_ERR_NULL = -1,      /* a required pointer is NULL                          */
+  MLASD_ERR_SHAPE = -2,     /* a size, shape, stride or dtype is not accepted     */
+  MLASD_ERR_ALIGN = -3,     /* a pointer or stride breaks the stated alignment    */
+  MLASD_ERR_VALUE = -4,     /* a scalar argument is invalid (non-finite scale)     */
   MLASD_ERR_HIP = -5,       /* a HIP runtime call failed (see mlasd_last_hip_error) */
-  MLASD_ERR_DEVICE = -6,    /* the current device is not a gfx950 device          */
-  MLASD_ERR_CAPTURE = -7    /* split scratch would have to grow during graph capture */
+  MLASD_ERR_DEVICE = -6,    /* the current device is not a gfx950 device           */
+  MLASD_ERR_CAPTURE = -7,   /* an allocating call was made while capturing         */
+  MLASD_ERR_WORKSPACE = -8  /* the call's plan needs more split scratch than was
+                               reserved for the stream (mlasd_prepare / reserve) */
 };
+
+/* Element types of mlasd_tensor. */
+enum { MLASD_U8 = 1, MLASD_I32 = 2, MLASD_BF16 = 3, MLASD_F32 = 4 };
+
+/* A strided view of device memory.  Element (i0, i1, ...) lives at
+ * data + sum_k i_k * stride[k] elements.  Only the first ndim entries of
+ * shape and stride are read. */
+typedef struct mlasd_tensor {
+  void* data;
+  int32_t dtype;       /* MLASD_U8, MLASD_I32, MLASD_BF16 or MLASD_F32 */
+  int32_t ndim;        /* 1..4 */
+  int64_t shape[4];
+  int64_t stride[4];   /* in elements, >= 0 */
+} mlasd_tensor;
 
 /* Fixed shape of the method. */
 #define MLASD_HEADS 64
@@ -77,39 +95,42 @@ enum {
 #define MLASD_PAGE_BYTES 149504
 
 /*
- * mla_sparse_decode -- the decode hot path.
+ * mla_sparse_decode -- the decode hot path (the step of "The Turning
+ * Point", "The Reasoning Process", Steps 1-5, with the outputs of "The
+ * Moment of Validation", "Two Failures, Two Lessons").
  *
- *   q          bf16 [batch, 64, 512]; 16-byte aligned.  Dims 0..447 nope,
- *              448..511 rope ("The Turning Point", Step 1).
- *   kv_pages   uint8 [num_pages, 149504]; 16-byte aligned; num_pages >= 1.
- *   page_table int32 [batch, max_pages]; max_pages >= 1; logical page ->
- *              physical page of each sequence.
- *   topk_idx   int32 [batch, topk]; 0 <= topk <= 512; token positions in the
- *              sequence; -1 or any out-of-range value is masked.
- *   seq_lens   int32 [batch].
+ *   q          BF16 [B, 64, 512]; dims 0..447 nope, 448..511 rope ("The
+ *              Turning Point", Step 1).  data 16-byte aligned, stride[0] and
+ *              stride[1] multiples of 8.
+ *   kv_pages   U8 [num_pages, 149504], num_pages >= 1; stride[0] >= 149504
+ *              and a multiple of 16; data 16-byte aligned.
+ *   page_table I32 [B, max_pages], max_pages >= 1: logical page -> physical
+ *              page of each query's sequence.  Any stride[0].
+ *   topk_idx   I32 [B, topk], 0 <= topk <= 512: token positions; -1 or any
+ *              out-of-range value is masked.  Any stride[0].
+ *   seq_lens   I32 [B].  Any stride.
  *   softmax_scale  finite float multiplying every score.
- *   out        bf16 [batch, 64, 448] (written, round-to-nearest-even);
- *              8-byte aligned.
- *   lse        float32 [batch, 64] (written, natural log).
+ *   out        BF16 [B, 64, 448] (written, round-to-nearest-even); data
+ *              16-byte aligned, stride[0] and stride[1] multiples of 8.
+ *   lse        F32 [B, 64] (written, natural log).  Any stride[0].
  *   stream     HIP stream to enqueue on.
  *
- * batch == 0 is a no-op.  topk == 0 writes out = 0, lse = -inf.
+ * B == 0 is a no-op.  topk == 0 writes out = 0, lse = -inf.
+ * When the plan cuts a query's top-k list into slices (small batches), the
+ * fp32 partial results live in the split scratch reserved for `stream` by
+ * mlasd_prepare (or mlasd_reserve); if that scratch is missing or too small
+ * the call returns MLASD_ERR_WORKSPACE and enqueues nothing.  It never
+ * allocates, frees or synchronises, so it may be captured into a graph.
  * Numerics: the 448 nope dims of q and K, and the value rows, enter the
  * contractions in fp16; the 64 rope dims in bf16; sums and the softmax are
- * fp32.  Dequantised cache values are exact in fp16 while their magnitude is
- * below 65520 and they are multiples of 2^-24 (UE8M0 exponents -15..7 for
- * e4m3 bytes); q's nope values are exact in fp16 for magnitudes in
- * [2^-14, 65504] and keep every bit down to 2^-24 below that.  Larger values
- * overflow to infinity.
+ * fp32.  Dequantised cache values are exact in fp16 for UE8M0 bytes
+ * 112..134; q's nope values for magnitudes in [2^-14, 65504].
  * Returns MLASD_OK or a negative MLASD_ERR_* code.
  */
-int mla_sparse_decode(const void* q,
-                      const void* kv_pages, int64_t num_pages,
-                      const int32_t* page_table, int32_t max_pages,
-                      const int32_t* topk_idx, int32_t topk,
-                      const int32_t* seq_lens, int32_t batch,
-                      float softmax_scale,
-                      void* out, float* lse,
+int mla_sparse_decode(const mlasd_tensor* q, const mlasd_tensor* kv_pages,
+                      const mlasd_tensor* page_table, const mlasd_tensor* topk_idx,
+                      const mlasd_tensor* seq_lens, float softmax_scale,
+                      const mlasd_tensor* out, const mlasd_tensor* lse,
                       mlasd_stream_t stream);
 
 /*
@@ -125,17 +146,14 @@ int mla_sparse_decode(const void* q,
  *                Other values: MLASD_ERR_SHAPE.
  * Results equal mla_sparse_decode's up to floating-point rounding (the head
  * groups do not change any value; the slices change the summation order).
- * Intended for tests and benchmarks.
+ * Split plans need scratch as mla_sparse_decode does; mla_sparse_workspace_size
+ * gives the bytes for mlasd_reserve.  Intended for tests and benchmarks.
  */
-int mla_sparse_decode_ex(const void* q,
-                         const void* kv_pages, int64_t num_pages,
-                         const int32_t* page_table, int32_t max_pages,
-                         const int32_t* topk_idx, int32_t topk,
-                         const int32_t* seq_lens, int32_t batch,
-                         float softmax_scale,
-                         void* out, float* lse,
-                         int32_t nsplit, int32_t head_groups,
-                         mlasd_stream_t stream);
+int mla_sparse_decode_ex(const mlasd_tensor* q, const mlasd_tensor* kv_pages,
+                         const mlasd_tensor* page_table, const mlasd_tensor* topk_idx,
+                         const mlasd_tensor* seq_lens, float softmax_scale,
+                         const mlasd_tensor* out, const mlasd_tensor* lse,
+                         int32_t nsplit, int32_t head_groups, mlasd_stream_t stream);
 
 /*
  * mla_sparse_plan -- the plan the library would use (host only, no device
@@ -149,26 +167,31 @@ int mla_sparse_plan(int32_t batch, int32_t topk, int32_t nsplit_request, int32_t
                     int32_t* nsplit, int32_t* split_len, int32_t* head_groups);
 
 /*
+ * mla_sparse_workspace_size -- bytes of split scratch a decode of this shape
+ * needs (host only): 0 when the plan does not split.  nsplit and
+ * head_groups as in mla_sparse_decode_ex (0 = automatic); num_cus as in
+ * mla_sparse_plan.
+ */
+int mla_sparse_workspace_size(int32_t batch, int32_t topk, int32_t nsplit, int32_t head_groups,
+                              int32_t num_cus, size_t* bytes);
+
+/*
  * mla_sparse_gather_dequant -- test hook for the gather + dequant stage:
- * runs the same index resolution, page-table walk, gather and dequantisation
- * code as the decode kernel and writes what the contractions consume.
+ * runs the decode kernel's own index resolution, page-table walk, gather and
+ * dequantisation, and writes each entry's key row as the contractions
+ * consume it (its first 448 values are also the value row).
  *
- *   k_rows  bf16 [batch, topk, 512]: key row of each entry as the QK^T
- *           contraction consumes it: nope e4m3 * 2^(e-127) rounded to fp16
- *           (as in v_rows) and written widened to bf16, which is exact;
- *           rope as stored.  Zero for masked entries.
- *   v_rows  fp16 [batch, topk, 448]: the value row of each entry as the PV
- *           contraction consumes it (fp16; exact while every dequantised
- *           value is a multiple of 2^-24 of magnitude <= 65504).  Zero for
- *           masked entries.
- *   valid   uint8 [batch, topk]: 1 where the entry is valid.
+ *   rows   F32 [B, topk, 512], innermost contiguous, data 16-byte aligned,
+ *          stride[0] and stride[1] multiples of 4: nope dims are the
+ *          dequantised values e4m3 * 2^(e-127) exactly as the kernel holds
+ *          them (widened to fp32, which is exact), rope dims the stored bf16
+ *          values.  Zero for masked entries.
+ *   valid  U8 [B, topk]: 1 where the entry is valid.  Any stride[0].
  * Other arguments as in mla_sparse_decode.
  */
-int mla_sparse_gather_dequant(const void* kv_pages, int64_t num_pages,
-                              const int32_t* page_table, int32_t max_pages,
-                              const int32_t* topk_idx, int32_t topk,
-                              const int32_t* seq_lens, int32_t batch,
-                              void* k_rows, void* v_rows, uint8_t* valid,
+int mla_sparse_gather_dequant(const mlasd_tensor* kv_pages, const mlasd_tensor* page_table,
+                              const mlasd_tensor* topk_idx, const mlasd_tensor* seq_lens,
+                              const mlasd_tensor* rows, const mlasd_tensor* valid,
                               mlasd_stream_t stream);
 
 /*
@@ -177,12 +200,12 @@ int mla_sparse_gather_dequant(const void* kv_pages, int64_t num_pages,
  * FP8/UE8M0 bullet; layout as above, "The Validation Gate", "The Test
  * Design").
  *
- *   latent     bf16 [n_tokens, 512]; 16-byte aligned.  Dims 0..447 nope,
- *              448..511 rope.
- *   seq_ids    int32 [n_tokens]: page-table row of each token.
- *   positions  int32 [n_tokens]: position of each token in its sequence.
- *   page_table int32 [batch, max_pages]; logical page -> physical page.
- *   kv_pages   uint8 [num_pages, 149504]; 16-byte aligned; written.
+ *   latent     BF16 [N, 512]; dims 0..447 nope, 448..511 rope.  data
+ *              16-byte aligned, stride[0] a multiple of 8.
+ *   seq_ids    I32 [N]: page-table row of each token.  Any stride.
+ *   positions  I32 [N]: position of each token in its sequence.  Any stride.
+ *   page_table I32 [B, max_pages], B >= 1, max_pages >= 1.  Any stride[0].
+ *   kv_pages   U8 [num_pages, 149504] as for the decode; written.
  *
  * Token i goes to page page_table[s][p / 256], slot p % 256 (s = seq_ids[i],
  * p = positions[i]).  Nope dims of group g (64 each) get scale byte
@@ -190,38 +213,49 @@ int mla_sparse_gather_dequant(const void* kv_pages, int64_t num_pages,
  * [-127, 127] (0 -> -127), and codes e4m3(round-to-nearest-even(x * 2^-k));
  * scale byte 7 is 0; rope values are stored as they are.  Tokens whose
  * sequence, position or page is out of range are skipped (not an error).
- * Two tokens with the same destination in one call: either may win.
- * n_tokens == 0 is a no-op.  Returns MLASD_OK or a negative MLASD_ERR_* code.
+ * Tokens of one call must have distinct destinations: two tokens with the
+ * same destination leave an undefined record there (their byte stores may
+ * interleave).  N == 0 is a no-op.  Returns MLASD_OK or a negative
+ * MLASD_ERR_* code.
  */
-int mla_kv_append(const void* latent, const int32_t* seq_ids, const int32_t* positions,
-                  int32_t n_tokens, const int32_t* page_table, int32_t batch, int32_t max_pages,
-                  void* kv_pages, int64_t num_pages, mlasd_stream_t stream);
+int mla_kv_append(const mlasd_tensor* latent, const mlasd_tensor* seq_ids,
+                  const mlasd_tensor* positions, const mlasd_tensor* page_table,
+                  const mlasd_tensor* kv_pages, mlasd_stream_t stream);
 
 /*
  * mlasd_prepare -- reserve the split scratch of `stream` (on the current
  * device) for every automatically planned mla_sparse_decode call with
- * batch <= max_batch and topk <= max_topk, so that such calls made later
- * under graph capture allocate nothing.  Everything a captured call needs
+ * batch <= max_batch and topk <= max_topk.  Everything a captured call needs
  * must exist before capture begins ("The Validation Moment", "The Weight of
- * 'CUDA Graph Capture Completed Without Errors'").  Forced plans
- * (mla_sparse_decode_ex) may need more.  Host call; may allocate and
- * synchronise the stream; refused with MLASD_ERR_CAPTURE while the stream
- * is capturing and the scratch would have to grow.  max_batch == 0 reserves
- * nothing.  Errors: MLASD_ERR_SHAPE (negative sizes, max_topk > 512),
- * MLASD_ERR_DEVICE, MLASD_ERR_HIP.
+ * 'CUDA Graph Capture Completed Without Errors'").  Host call; may allocate
+ * (hipMalloc) and zero the new scratch; refused with MLASD_ERR_CAPTURE
+ * while the stream is capturing.  Scratch only grows: when it must, the new
+ * buffer replaces the old one for later calls, and the old one stays
+ * allocated until mlasd_release, so graphs captured earlier stay valid.
+ * max_batch == 0 reserves nothing.  Errors: MLASD_ERR_SHAPE (negative sizes,
+ * max_topk > 512), MLASD_ERR_DEVICE, MLASD_ERR_HIP.
  */
 int mlasd_prepare(mlasd_stream_t stream, int32_t max_batch, int32_t max_topk);
 
+/* mlasd_reserve -- as mlasd_prepare, for at least `bytes` of split scratch
+ * (e.g. mla_sparse_workspace_size of a forced plan). */
+int mlasd_reserve(mlasd_stream_t stream, size_t bytes);
+
 /*
- * mlasd_release -- synchronise `stream` and free its split scratch on the
- * current device (a no-op if it has none).  Refused with MLASD_ERR_CAPTURE
- * while the stream is capturing.  A later call reserves scratch again.
- * Graphs captured while the freed scratch was in use must not be replayed
+ * mlasd_release -- synchronise `stream` and free all of its split scratch
+ * on the current device, superseded buffers included (a no-op if it has
+ * none).  Refused with MLASD_ERR_CAPTURE while the stream is capturing.
+ * Graphs captured while any of that scratch was in use must not be replayed
  * afterwards.
+ *
+ * Sharing: the scratch belongs to (device, stream).  Calls enqueued on one
+ * stream are ordered; a graph captured on stream S uses S's scratch
+ * wherever it is replayed, so its replays must be ordered with other work
+ * that uses S's scratch (eager calls on S, other graphs captured on S).
  */
 int mlasd_release(mlasd_stream_t stream);
 
-/* Bytes of split scratch currently held for `stream` on the current device. */
+/* Bytes of split scratch currently usable by calls on `stream` (current device). */
 int mlasd_workspace_bytes(mlasd_stream_t stream, size_t* bytes);
 
 /* Static text for a status code. */

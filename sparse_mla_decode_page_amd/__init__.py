@@ -5,6 +5,8 @@ The decode runs in hand-written HIP kernels behind a C ABI
 """
 from ._binding import (  # noqa: F401
     MlasdError,
+    Tensor,
+    describe,
     library_path,
     load_library,
     mla_kv_append,
@@ -13,9 +15,12 @@ from ._binding import (  # noqa: F401
     plan,
     prepare,
     release,
+    reserve,
     status_string,
     workspace_bytes,
+    workspace_size,
 )
 
 __all__ = ["mla_sparse_decode", "mla_sparse_gather_dequant", "mla_kv_append", "plan", "prepare",
-           "release", "workspace_bytes", "load_library", "library_path", "status_string", "MlasdError"]
+           "reserve", "release", "workspace_bytes", "workspace_size", "describe", "Tensor",
+           "load_library", "library_path", "status_string", "MlasdError"]

@@ -1,9 +1,11 @@
 """ctypes binding for libmlasd.so (argument marshalling only).
 
 Every step of the decode runs in the HIP kernels behind the C ABI declared in
-include/mlasd.h; this module only checks tensor dtypes/shapes, picks the
-stream and forwards raw device pointers.  There is no fallback: if the
-library is not built, or a call fails, it raises.
+include/mlasd.h; this module only turns torch tensors into mlasd_tensor
+descriptors (pointer, dtype, shape, strides), picks the stream and forwards
+the call.  Shape, stride and alignment rules are checked by the library
+itself.  There is no fallback: if the library is not built, or a call
+fails, it raises.
 """
 from __future__ import annotations
 
@@ -20,12 +22,23 @@ D_V = 448
 MAX_TOPK = 512
 PAGE_BYTES = 149504
 
+STATUS_WORKSPACE = -8
 _STATUS_OK = 0
 _lib = None
 
+_DTYPES = {torch.uint8: 1, torch.int32: 2, torch.bfloat16: 3, torch.float32: 4}
+
 
 class MlasdError(RuntimeError):
-    pass
+    def __init__(self, msg, status=None):
+        super().__init__(msg)
+        self.status = status
+
+
+class Tensor(ctypes.Structure):
+    """mlasd_tensor: device pointer, dtype, ndim, shape[4], stride[4] (elements)."""
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
 
 
 def library_path() -> str:
@@ -41,25 +54,23 @@ def load_library():
         raise MlasdError(f"{LIB_PATH} not found: build it first "
                          "(python -m sparse_mla_decode_page_amd._build)")
     lib = ctypes.CDLL(LIB_PATH)
-    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
-    common = [vp, vp, i64, vp, i32, vp, i32, vp, i32, f32, vp, vp]
-    lib.mla_sparse_decode.argtypes = common + [vp]
-    lib.mla_sparse_decode.restype = ctypes.c_int
-    lib.mla_sparse_decode_ex.argtypes = common + [i32, i32, vp]
-    lib.mla_sparse_decode_ex.restype = ctypes.c_int
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    T = ctypes.POINTER(Tensor)
+    lib.mla_sparse_decode.argtypes = [T, T, T, T, T, f32, T, T, vp]
+    lib.mla_sparse_decode_ex.argtypes = [T, T, T, T, T, f32, T, T, i32, i32, vp]
     lib.mla_sparse_plan.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                     ctypes.POINTER(i32)]
-    lib.mla_sparse_plan.restype = ctypes.c_int
-    lib.mla_sparse_gather_dequant.argtypes = [vp, i64, vp, i32, vp, i32, vp, i32, vp, vp, vp, vp]
-    lib.mla_sparse_gather_dequant.restype = ctypes.c_int
-    lib.mla_kv_append.argtypes = [vp, vp, vp, i32, vp, i32, i32, vp, i64, vp]
-    lib.mla_kv_append.restype = ctypes.c_int
+    lib.mla_sparse_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.mla_sparse_gather_dequant.argtypes = [T, T, T, T, T, T, vp]
+    lib.mla_kv_append.argtypes = [T, T, T, T, T, vp]
     lib.mlasd_prepare.argtypes = [vp, i32, i32]
-    lib.mlasd_prepare.restype = ctypes.c_int
+    lib.mlasd_reserve.argtypes = [vp, sz]
     lib.mlasd_release.argtypes = [vp]
-    lib.mlasd_release.restype = ctypes.c_int
-    lib.mlasd_workspace_bytes.argtypes = [vp, ctypes.POINTER(ctypes.c_size_t)]
-    lib.mlasd_workspace_bytes.restype = ctypes.c_int
+    lib.mlasd_workspace_bytes.argtypes = [vp, ctypes.POINTER(sz)]
+    for name in ("mla_sparse_decode", "mla_sparse_decode_ex", "mla_sparse_plan",
+                 "mla_sparse_workspace_size", "mla_sparse_gather_dequant", "mla_kv_append",
+                 "mlasd_prepare", "mlasd_reserve", "mlasd_release", "mlasd_workspace_bytes"):
+        getattr(lib, name).restype = ctypes.c_int
     lib.mlasd_status_string.argtypes = [ctypes.c_int]
     lib.mlasd_status_string.restype = ctypes.c_char_p
     lib.mlasd_last_hip_error.argtypes = []
@@ -80,30 +91,48 @@ def _check(rc: int, what: str):
         extra = ""
         if rc == -5:
             extra = f" (hip error {lib.mlasd_last_hip_error()})"
-        raise MlasdError(f"{what}: {status_string(rc)}{extra} [{rc}]")
+        raise MlasdError(f"{what}: {status_string(rc)}{extra} [{rc}]", rc)
 
 
-def _ptr(t):
-    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
-
-
-def _need(t, name, dtype, ndim):
+def describe(t) -> Tensor:
+    """mlasd_tensor descriptor of a torch tensor (no copy, no checks: the
+    library validates dtype, shape, strides and alignment)."""
     if not isinstance(t, torch.Tensor):
-        raise TypeError(f"{name} must be a torch.Tensor")
-    if t.dtype != dtype:
-        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if t.dim() != ndim:
-        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+        raise TypeError("expected a torch.Tensor")
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    if t.dim() > 4 or t.dim() < 1:
+        raise ValueError(f"tensor rank {t.dim()} not supported")
+    d = Tensor()
+    d.data = t.data_ptr() if t.numel() > 0 else 0
+    d.dtype = _DTYPES[t.dtype]
+    d.ndim = t.dim()
+    for k in range(t.dim()):
+        d.shape[k] = t.shape[k]
+        d.stride[k] = t.stride(k)
+    return d
+
+
+def _same_device(*ts):
+    dev = None
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("all tensors must be device tensors")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+    return dev
 
 
 def _stream(stream, device):
     if stream is None:
         stream = torch.cuda.current_stream(device)
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _device(device):
+    return torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
 
 
 def plan(batch: int, topk: int, nsplit: int = 0, num_cus: int = 0):
@@ -115,19 +144,35 @@ def plan(batch: int, topk: int, nsplit: int = 0, num_cus: int = 0):
     return a.value, b.value, c.value
 
 
+def workspace_size(batch: int, topk: int, nsplit: int = 0, head_groups: int = 0, num_cus: int = 0) -> int:
+    """Bytes of split scratch a decode of this shape and plan needs."""
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    _check(lib.mla_sparse_workspace_size(batch, topk, nsplit, head_groups, num_cus, ctypes.byref(n)),
+           "mla_sparse_workspace_size")
+    return n.value
+
+
 def prepare(max_batch: int, max_topk: int = MAX_TOPK, stream=None, device=None):
     """Reserve the split scratch of `stream` for every automatically planned
-    decode with batch <= max_batch and topk <= max_topk (call before graph
-    capture)."""
-    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    decode with batch <= max_batch and topk <= max_topk (before graph capture)."""
+    dev = _device(device)
     lib = load_library()
     with torch.cuda.device(dev):
         _check(lib.mlasd_prepare(_stream(stream, dev), max_batch, max_topk), "mlasd_prepare")
 
 
+def reserve(nbytes: int, stream=None, device=None):
+    """Reserve at least `nbytes` of split scratch for `stream`."""
+    dev = _device(device)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        _check(lib.mlasd_reserve(_stream(stream, dev), nbytes), "mlasd_reserve")
+
+
 def release(stream=None, device=None):
     """Free the split scratch of `stream` (synchronises the stream)."""
-    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    dev = _device(device)
     lib = load_library()
     with torch.cuda.device(dev):
         _check(lib.mlasd_release(_stream(stream, dev)), "mlasd_release")
@@ -135,7 +180,7 @@ def release(stream=None, device=None):
 
 def workspace_bytes(stream=None, device=None) -> int:
     """Bytes of split scratch the library holds for `stream`."""
-    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    dev = _device(device)
     lib = load_library()
     n = ctypes.c_size_t(0)
     with torch.cuda.device(dev):
@@ -143,50 +188,29 @@ def workspace_bytes(stream=None, device=None) -> int:
     return n.value
 
 
-def _check_cache_args(kv_pages, page_table, topk_idx, seq_lens):
-    _need(kv_pages, "kv_pages", torch.uint8, 2)
-    _need(page_table, "page_table", torch.int32, 2)
-    _need(topk_idx, "topk_idx", torch.int32, 2)
-    _need(seq_lens, "seq_lens", torch.int32, 1)
-    if kv_pages.shape[1] != PAGE_BYTES:
-        raise ValueError(f"kv_pages rows must be {PAGE_BYTES} bytes")
-    B = seq_lens.shape[0]
-    if page_table.shape[0] != B or topk_idx.shape[0] != B:
-        raise ValueError("page_table / topk_idx / seq_lens batch mismatch")
-    dev = kv_pages.device
-    for t in (page_table, topk_idx, seq_lens):
-        if t.device != dev:
-            raise ValueError("all tensors must be on the same device")
-    return B
-
-
 def mla_sparse_decode(q, kv_pages, page_table, topk_idx, seq_lens, softmax_scale,
                       out=None, lse=None, stream=None, nsplit=None, head_groups=None):
     """Sparse MLA decode.  Returns (out bf16 [B,64,448], lse f32 [B,64]).
 
-    q bf16 [B,64,512]; kv_pages uint8 [num_pages,149504]; page_table int32
-    [B,max_pages]; topk_idx int32 [B,topk]; seq_lens int32 [B].  `nsplit`
-    forces the number of top-k slices per query and `head_groups` (1, 2, 4)
-    the number of workgroups sharing a slice's heads (None = library plan).
+    q bf16 [B,64,512]; kv_pages uint8 [num_pages,149504] (any page stride);
+    page_table int32 [B,max_pages]; topk_idx int32 [B,topk]; seq_lens int32
+    [B].  `nsplit` forces the number of top-k slices per query and
+    `head_groups` (1, 2, 4) the number of workgroups sharing a slice's heads
+    (None = library plan).  Split plans need scratch reserved with
+    prepare() / reserve() on the stream first.
     """
-    B = _check_cache_args(kv_pages, page_table, topk_idx, seq_lens)
-    _need(q, "q", torch.bfloat16, 3)
-    if tuple(q.shape) != (B, HEADS, D_QK):
-        raise ValueError(f"q must be [{B},{HEADS},{D_QK}], got {tuple(q.shape)}")
-    dev = q.device
+    dev = _same_device(q, kv_pages, page_table, topk_idx, seq_lens)
+    B = seq_lens.shape[0] if seq_lens.dim() == 1 else -1
     if out is None:
         out = torch.empty((B, HEADS, D_V), dtype=torch.bfloat16, device=dev)
     if lse is None:
         lse = torch.empty((B, HEADS), dtype=torch.float32, device=dev)
-    _need(out, "out", torch.bfloat16, 3)
-    _need(lse, "lse", torch.float32, 2)
-    if tuple(out.shape) != (B, HEADS, D_V) or tuple(lse.shape) != (B, HEADS):
-        raise ValueError("out / lse shape mismatch")
+    _same_device(out, lse, q)
     lib = load_library()
+    descs = [describe(t) for t in (q, kv_pages, page_table, topk_idx, seq_lens)]
+    do, dl = describe(out), describe(lse)
     with torch.cuda.device(dev):
-        args = (_ptr(q), _ptr(kv_pages), kv_pages.shape[0], _ptr(page_table), page_table.shape[1],
-                _ptr(topk_idx), topk_idx.shape[1], _ptr(seq_lens), B, float(softmax_scale),
-                _ptr(out), _ptr(lse))
+        args = [ctypes.byref(d) for d in descs] + [float(softmax_scale), ctypes.byref(do), ctypes.byref(dl)]
         if nsplit is None and head_groups is None:
             rc = lib.mla_sparse_decode(*args, _stream(stream, dev))
         else:
@@ -197,48 +221,27 @@ def mla_sparse_decode(q, kv_pages, page_table, topk_idx, seq_lens, softmax_scale
 
 
 def mla_sparse_gather_dequant(kv_pages, page_table, topk_idx, seq_lens, stream=None):
-    """Test hook: (k_rows bf16 [B,topk,512], v_rows fp16 [B,topk,448], valid uint8 [B,topk])
-    exactly as the decode kernel's gather + dequant stage produces them."""
-    B = _check_cache_args(kv_pages, page_table, topk_idx, seq_lens)
-    dev = kv_pages.device
-    K = topk_idx.shape[1]
-    k_rows = torch.empty((B, K, D_QK), dtype=torch.bfloat16, device=dev)
-    v_rows = torch.empty((B, K, D_V), dtype=torch.float16, device=dev)
+    """Test hook: (rows f32 [B,topk,512], valid uint8 [B,topk]) exactly as the
+    decode kernel's gather + dequant stage holds them."""
+    dev = _same_device(kv_pages, page_table, topk_idx, seq_lens)
+    B, K = topk_idx.shape[0], topk_idx.shape[1]
+    rows = torch.empty((B, K, D_QK), dtype=torch.float32, device=dev)
     valid = torch.empty((B, K), dtype=torch.uint8, device=dev)
     lib = load_library()
+    descs = [describe(t) for t in (kv_pages, page_table, topk_idx, seq_lens, rows, valid)]
     with torch.cuda.device(dev):
-        rc = lib.mla_sparse_gather_dequant(_ptr(kv_pages), kv_pages.shape[0], _ptr(page_table),
-                                           page_table.shape[1], _ptr(topk_idx), K, _ptr(seq_lens), B,
-                                           _ptr(k_rows), _ptr(v_rows), _ptr(valid),
-                                           _stream(stream, dev))
+        rc = lib.mla_sparse_gather_dequant(*[ctypes.byref(d) for d in descs], _stream(stream, dev))
     _check(rc, "mla_sparse_gather_dequant")
-    return k_rows, v_rows, valid
+    return rows, valid
 
 
 def mla_kv_append(latent, seq_ids, positions, page_table, kv_pages, stream=None):
     """Quantise token latents (bf16 [N, 512]) into the paged cache in place.
     seq_ids / positions int32 [N]; page_table int32 [B, max_pages]."""
-    _need(latent, "latent", torch.bfloat16, 2)
-    _need(seq_ids, "seq_ids", torch.int32, 1)
-    _need(positions, "positions", torch.int32, 1)
-    _need(page_table, "page_table", torch.int32, 2)
-    _need(kv_pages, "kv_pages", torch.uint8, 2)
-    n = latent.shape[0]
-    if latent.shape[1] != D_QK:
-        raise ValueError(f"latent must be [N, {D_QK}]")
-    if seq_ids.shape[0] != n or positions.shape[0] != n:
-        raise ValueError("seq_ids / positions must have one entry per token")
-    if kv_pages.shape[1] != PAGE_BYTES:
-        raise ValueError(f"kv_pages rows must be {PAGE_BYTES} bytes")
-    dev = kv_pages.device
-    for t in (latent, seq_ids, positions, page_table):
-        if t.device != dev:
-            raise ValueError("all tensors must be on the same device")
+    dev = _same_device(latent, seq_ids, positions, page_table, kv_pages)
     lib = load_library()
+    descs = [describe(t) for t in (latent, seq_ids, positions, page_table, kv_pages)]
     with torch.cuda.device(dev):
-        rc = lib.mla_kv_append(_ptr(latent), _ptr(seq_ids), _ptr(positions), n, _ptr(page_table),
-                               page_table.shape[0], page_table.shape[1], _ptr(kv_pages),
-                               kv_pages.shape[0], _stream(stream, dev))
+        rc = lib.mla_kv_append(*[ctypes.byref(d) for d in descs], _stream(stream, dev))
     _check(rc, "mla_kv_append")
     return kv_pages
-

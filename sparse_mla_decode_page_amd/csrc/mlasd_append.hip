@@ -39,18 +39,18 @@ __global__ __launch_bounds__(64 * kAppendWaves) void mla_kv_append_kernel(const 
   // The latent row is issued first so its latency overlaps the dependent
   // seq id -> page table lookups.  Lanes 0..55: 8 nope values; lanes 56..63:
   // 8 rope values (bf16 bits).  Nothing here is read again: stream it.
-  const u32x4 w = __builtin_nontemporal_load((const u32x4*)(p.latent + (int64_t)tok * kDQK) + lane);
+  const u32x4 w = __builtin_nontemporal_load((const u32x4*)(p.latent + (int64_t)tok * p.lat_s) + lane);
   // Validity, wave-uniform and branch-free up to one exit so the compiler
   // keeps the latent load above it: the page-table lookup is clamped to
   // entry 0 (batch >= 1 and max_pages >= 1) when the token is out of range.
-  const int s = p.seq_ids[tok], pos = p.positions[tok];
+  const int s = p.seq_ids[(int64_t)tok * p.seq_s], pos = p.positions[(int64_t)tok * p.pos_s];
   const bool in_table = s >= 0 && s < p.batch && pos >= 0 && (pos >> 8) < p.max_pages;
-  const int64_t entry = in_table ? (int64_t)s * p.max_pages + (pos >> 8) : 0;
+  const int64_t entry = in_table ? (int64_t)s * p.pt_sb + (pos >> 8) : 0;
   const int looked_up = p.page_table[entry];
   const int page = in_table ? looked_up : -1;
   if (page < 0 || (int64_t)page >= p.num_pages) return;
   const int slot = pos & (kPageTokens - 1);
-  uint8_t* pbase = p.kv + (int64_t)page * kPageBytes;
+  uint8_t* pbase = p.kv + (int64_t)page * p.page_stride;
 
   float v[8];
 #pragma unroll

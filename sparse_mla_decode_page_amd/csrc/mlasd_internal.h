@@ -21,22 +21,30 @@ constexpr int64_t kScaleBase = 147456;
 
 // Kernel tiling.
 constexpr int kTileTokens = 32;   // tokens per LDS tile
-constexpr int kThreads = 512;     // 8 waves: 4 consumers + 4 producers
+constexpr int kThreads = 512;     // 8 waves per decode workgroup
 
+// Strides are in elements of the tensor's own type.
 struct DecodeParams {
   const uint16_t* q;          // bf16 [B, 64, 512]
-  const uint8_t* kv;          // [num_pages, 149504]
+  int64_t q_sb, q_sh;
+  const uint8_t* kv;          // [num_pages, >= 149504]
   int64_t num_pages;
+  int64_t page_stride;        // bytes between pages
   const int32_t* page_table;  // [B, max_pages]
+  int64_t pt_sb;
   int32_t max_pages;
   const int32_t* topk_idx;    // [B, topk]
+  int64_t idx_sb;
   int32_t topk;
   const int32_t* seq_lens;    // [B]
+  int64_t len_s;
   int32_t batch;
   float scale_log2;           // softmax_scale * log2(e)
   uint16_t* out;              // bf16 [B, 64, 448]
+  int64_t out_sb, out_sh;
   float* lse;                 // [B, 64]
-  float* part_o;              // [B, nsplit, 64, 448] when nsplit > 1
+  int64_t lse_sb;
+  float* part_o;              // [B, nsplit, 64, 448] when nsplit > 1 (contiguous scratch)
   float* part_lse;            // [B, nsplit, 64]      when nsplit > 1
   int32_t nsplit;
   int32_t split_len;          // index entries per slice, multiple of kTileTokens
@@ -46,29 +54,39 @@ struct DecodeParams {
 struct GatherParams {
   const uint8_t* kv;
   int64_t num_pages;
+  int64_t page_stride;
   const int32_t* page_table;
+  int64_t pt_sb;
   int32_t max_pages;
   const int32_t* topk_idx;
+  int64_t idx_sb;
   int32_t topk;
   const int32_t* seq_lens;
+  int64_t len_s;
   int32_t batch;
-  uint16_t* k_rows;   // bf16 [B, topk, 512]
-  uint16_t* v_rows;   // fp16 [B, topk, 448]
+  float* rows;        // fp32 [B, topk, 512]
+  int64_t rows_sb, rows_sj;
   uint8_t* valid;     // [B, topk]
+  int64_t valid_sb;
   int32_t nsplit;
   int32_t split_len;
 };
 
 struct AppendParams {
   const uint16_t* latent;     // bf16 [n_tokens, 512]: 448 nope, 64 rope
+  int64_t lat_s;
   const int32_t* seq_ids;     // [n_tokens] page-table row of each token
+  int64_t seq_s;
   const int32_t* positions;   // [n_tokens] position within its sequence
+  int64_t pos_s;
   int32_t n_tokens;
   const int32_t* page_table;  // [batch, max_pages]
+  int64_t pt_sb;
   int32_t batch;
   int32_t max_pages;
-  uint8_t* kv;                // [num_pages, 149504]
+  uint8_t* kv;                // [num_pages, >= 149504]
   int64_t num_pages;
+  int64_t page_stride;
 };
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);

@@ -196,8 +196,8 @@ __device__ __forceinline__ LaneOffset lane_offset(int lane) {
                    : LaneOffset{(uint32_t)kScaleRecordBytes, (uint32_t)kScaleBase};
 }
 
-__device__ __forceinline__ void load_tile(TileRegs& r, const Smem& sm, const uint8_t* kv, int tile,
-                                          int n_valid, LastRecord last, int pw, int lane,
+__device__ __forceinline__ void load_tile(TileRegs& r, const Smem& sm, const uint8_t* kv, int64_t pstride,
+                                          int tile, int n_valid, LastRecord last, int pw, int lane,
                                           LaneOffset lo) {
   const int c0 = tile * kTileTokens + kTokPerProducer * pw;
   // Lane l resolves token c0 + l/8 with one LDS read; token j's page and slot
@@ -212,10 +212,10 @@ __device__ __forceinline__ void load_tile(TileRegs& r, const Smem& sm, const uin
   for (int j = 0; j < kTokPerProducer; ++j) {
     const int pg = __builtin_amdgcn_readlane(page, 8 * j);
     const int sl = __builtin_amdgcn_readlane(slot, 8 * j);
-    const uint8_t* base = kv + (int64_t)pg * kPageBytes;
+    const uint8_t* base = kv + (int64_t)pg * pstride;
     r.rec[j] = *(const u32x2*)(base + (__umul24((uint32_t)sl, lo.mul) + lo.add));
   }
-  r.rope = *(const u32x4*)(kv + (int64_t)page * kPageBytes + slot * kRecordBytes + kDNope + 16 * (lane & 7));
+  r.rope = *(const u32x4*)(kv + (int64_t)page * pstride + slot * kRecordBytes + kDNope + 16 * (lane & 7));
 }
 
 // a3: dequantise one producer wave's 8 gathered tokens into LDS buffer `buf`.
@@ -309,12 +309,12 @@ __device__ __forceinline__ void store_out(const DecodeParams& p, uint8_t* stage,
       w.y = bf16x2_rne(oacc[mb][2] * inv, oacc[mb][3] * inv);
       *(u32x2*)(stage + col * kStageRowBytes + 2 * (16 * mb + 4 * g)) = w;
     }
-    uint8_t* obase = (uint8_t*)(p.out + ((int64_t)b * kHeads + head0) * kDV + dim0);
+    uint8_t* obase = (uint8_t*)(p.out + (int64_t)b * p.out_sb + (int64_t)head0 * p.out_sh + dim0);
     constexpr int kChunks = 2 * kBlocks;   // 16-byte chunks per row
 #pragma unroll
     for (int k = 0; k < kBlocks / 2; ++k) {   // 16 rows x 32 kBlocks bytes
       const int i = lane + 64 * k, row = i / kChunks, ch = i - kChunks * row;
-      *(u32x4*)(obase + row * (2 * kDV) + 16 * ch) = *(const u32x4*)(stage + row * kStageRowBytes + 16 * ch);
+      *(u32x4*)(obase + row * (2 * p.out_sh) + 16 * ch) = *(const u32x4*)(stage + row * kStageRowBytes + 16 * ch);
     }
   } else {
     const int64_t prow0 = ((int64_t)b * p.nsplit + s) * kHeads + head0;
@@ -353,8 +353,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
   const int e0 = s * p.split_len;
   const int n_ent = max(0, min(p.topk - e0, p.split_len));
 
-  const int n_valid = compact_slice(sm, p.topk_idx + (int64_t)b * p.topk + e0, n_ent,
-                                    p.seq_lens[b], p.page_table + (int64_t)b * p.max_pages,
+  const int n_valid = compact_slice(sm, p.topk_idx + (int64_t)b * p.idx_sb + e0, n_ent,
+                                    p.seq_lens[(int64_t)b * p.len_s], p.page_table + (int64_t)b * p.pt_sb,
                                     p.max_pages, p.num_pages);
   const int ntiles = (n_valid + kTileTokens - 1) / kTileTokens;
 
@@ -387,9 +387,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
       const LaneOffset lo = lane_offset(lane);
       TileRegs regs[kDepth];
 #pragma unroll
-      for (int u = 0; u < kDepth; ++u) load_tile(regs[u], sm, p.kv, u, n_valid, last, pw, lane, lo);
+      for (int u = 0; u < kDepth; ++u) load_tile(regs[u], sm, p.kv, p.page_stride, u, n_valid, last, pw, lane, lo);
       store_tile(sm, regs[0], 0, pw, lane);
-      load_tile(regs[0], sm, p.kv, kDepth, n_valid, last, pw, lane, lo);
+      load_tile(regs[0], sm, p.kv, p.page_stride, kDepth, n_valid, last, pw, lane, lo);
       __syncthreads();
       for (int t0 = 0; t0 < ntiles; t0 += kDepth) {
 #pragma unroll
@@ -400,7 +400,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
           // issued on every path, so the loads in flight behind each ring slot
           // are the same wherever it is consumed (past the end they re-read a
           // cached record)
-          load_tile(regs[nxt], sm, p.kv, t + 1 + kDepth, n_valid, last, pw, lane, lo);
+          load_tile(regs[nxt], sm, p.kv, p.page_stride, t + 1 + kDepth, n_valid, last, pw, lane, lo);
           if (t < ntiles) __syncthreads();
         }
       }
@@ -462,7 +462,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
   f16x8 qnope[kNopeSteps];
   bf16x8 qrope[2];
   {
-    const uint16_t* qrow = p.q + ((int64_t)b * kHeads + head) * kDQK + 8 * g;
+    const uint16_t* qrow = p.q + (int64_t)b * p.q_sb + (int64_t)head * p.q_sh + 8 * g;
     bf16x8 qb[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) qb[k] = *(const bf16x8*)(qrow + 32 * k);
@@ -598,7 +598,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
     store_out<kOBlocks>(p, (uint8_t*)&sm.kv[0][0] + wid * kStageBytes, oacc, inv, b, s, head0, 0, lane);
   if (g == 0) {
     if (p.nsplit == 1)
-      p.lse[(int64_t)b * kHeads + head] = lse_v;
+      p.lse[(int64_t)b * p.lse_sb + head] = lse_v;
     else
       p.part_lse[((int64_t)b * p.nsplit + s) * kHeads + head] = lse_v;
   }
@@ -651,9 +651,9 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(const Deco
     u32x2 w2;
     w2.x = bf16x2_rne(acc[0] * inv, acc[1] * inv);
     w2.y = bf16x2_rne(acc[2] * inv, acc[3] * inv);
-    *(u32x2*)(p.out + ((int64_t)b * kHeads + h) * kDV + 4 * c4) = w2;
+    *(u32x2*)(p.out + (int64_t)b * p.out_sb + (int64_t)h * p.out_sh + 4 * c4) = w2;
   }
-  if (c4 == 0) p.lse[(int64_t)b * kHeads + h] = tot > 0.f ? m + __logf(tot) : -INFINITY;
+  if (c4 == 0) p.lse[(int64_t)b * p.lse_sb + h] = tot > 0.f ? m + __logf(tot) : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -668,19 +668,19 @@ __global__ __launch_bounds__(kThreads, 1) void mla_gather_kernel(const GatherPar
   const int b = blk / p.nsplit, s = blk - b * p.nsplit;
   const int e0 = s * p.split_len;
   const int n_ent = max(0, min(p.topk - e0, p.split_len));
-  const int32_t* idx_row = p.topk_idx + (int64_t)b * p.topk + e0;
-  const int32_t* pt_row = p.page_table + (int64_t)b * p.max_pages;
-  const int seq_len = p.seq_lens[b];
+  const int32_t* idx_row = p.topk_idx + (int64_t)b * p.idx_sb + e0;
+  const int32_t* pt_row = p.page_table + (int64_t)b * p.pt_sb;
+  const int seq_len = p.seq_lens[(int64_t)b * p.len_s];
+  float* rows_b = p.rows + (int64_t)b * p.rows_sb;
 
   // masked entries: zero rows, valid = 0
   for (int j = tid; j < n_ent; j += kThreads) {
     int pg, sl;
     const bool v = resolve_entry(idx_row[j], seq_len, pt_row, p.max_pages, p.num_pages, pg, sl);
-    const int64_t e = (int64_t)b * p.topk + e0 + j;
-    p.valid[e] = v ? 1 : 0;
+    p.valid[(int64_t)b * p.valid_sb + e0 + j] = v ? 1 : 0;
     if (!v) {
-      for (int d = 0; d < kDQK; d += 8) *(u32x4*)(p.k_rows + e * kDQK + d) = u32x4{0, 0, 0, 0};
-      for (int d = 0; d < kDV; d += 8) *(u32x4*)(p.v_rows + e * kDV + d) = u32x4{0, 0, 0, 0};
+      float* r = rows_b + (int64_t)(e0 + j) * p.rows_sj;
+      for (int d = 0; d < kDQK; d += 4) *(f32x4*)(r + d) = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
 
@@ -690,27 +690,30 @@ __global__ __launch_bounds__(kThreads, 1) void mla_gather_kernel(const GatherPar
   for (int t = 0; t < ntiles; ++t) {
     if (wid >= kConsumers) {
       const LastRecord last = {sm.tok[n_valid - 1][0], sm.tok[n_valid - 1][1]};
-      load_tile(regs, sm, p.kv, t, n_valid, last, wid - kConsumers, lane, lane_offset(lane));
+      load_tile(regs, sm, p.kv, p.page_stride, t, n_valid, last, wid - kConsumers, lane, lane_offset(lane));
       store_tile(sm, regs, 0, wid - kConsumers, lane);
     }
     __syncthreads();
     for (int tt = wid; tt < kTileTokens; tt += kWaves) {
       const int ci = t * kTileTokens + tt;
       if (ci >= n_valid) continue;
-      const int64_t e = (int64_t)b * p.topk + e0 + sm.tok_entry[ci];
-      // the tile row as the contractions read it: fp16 nope (written out as V
-      // and, widened to bf16, as K) and bf16 rope
+      float* r = rows_b + (int64_t)(e0 + sm.tok_entry[ci]) * p.rows_sj;
+      // the tile row as the contractions read it: fp16 nope and bf16 rope,
+      // widened to fp32 (exact)
       const u32x4 raw = *(const u32x4*)&sm.kv[0][tt * kRow + 8 * lane];
-      u32x4 kq = raw;
+      f32x4 lo4, hi4;
       if (lane < 56) {
         const f16x8 h = __builtin_bit_cast(f16x8, raw);
-        kq.x = bf16x2_rne((float)h[0], (float)h[1]);
-        kq.y = bf16x2_rne((float)h[2], (float)h[3]);
-        kq.z = bf16x2_rne((float)h[4], (float)h[5]);
-        kq.w = bf16x2_rne((float)h[6], (float)h[7]);
-        *(u32x4*)(p.v_rows + e * kDV + 8 * lane) = raw;
+        lo4 = f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+        hi4 = f32x4{(float)h[4], (float)h[5], (float)h[6], (float)h[7]};
+      } else {
+        lo4 = f32x4{__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xffff0000u),
+                    __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xffff0000u)};
+        hi4 = f32x4{__uint_as_float(raw.z << 16), __uint_as_float(raw.z & 0xffff0000u),
+                    __uint_as_float(raw.w << 16), __uint_as_float(raw.w & 0xffff0000u)};
       }
-      *(u32x4*)(p.k_rows + e * kDQK + 8 * lane) = kq;
+      *(f32x4*)(r + 8 * lane) = lo4;
+      *(f32x4*)(r + 8 * lane + 4) = hi4;
     }
     __syncthreads();
   }

@@ -1,6 +1,9 @@
-"""Shared test helpers: device upload, tolerance checks, page-style report."""
+"""Shared test helpers: device upload, scratch reservation, tolerance checks,
+page-style report."""
 import numpy as np
 import torch
+
+import sparse_mla_decode_page_amd as mlasd
 
 # Tolerances for the attention outputs (bf16 out vs fp64 oracle): elementwise
 # |d| <= 2e-3 + 1e-2 * |ref| for out, |d| <= 1e-3 for lse.
@@ -17,6 +20,23 @@ def to_device(w, device="cuda"):
         topk_idx=torch.from_numpy(w.topk_idx).to(device),
         seq_lens=torch.from_numpy(w.seq_lens).to(device),
     )
+
+
+def reserve_for(batch, topk, nsplit=None, head_groups=None, stream=None):
+    """Reserve the split scratch a decode of this shape and plan needs on
+    `stream` (a host call: never inside graph capture)."""
+    n = mlasd.workspace_size(batch, topk, int(nsplit or 0), int(head_groups or 0))
+    if n:
+        mlasd.reserve(n, stream=stream)
+
+
+def decode(d, scale, nsplit=None, head_groups=None, stream=None, out=None, lse=None, reserve=True):
+    """mla_sparse_decode on uploaded tensors, reserving its scratch first."""
+    if reserve:
+        reserve_for(d["seq_lens"].shape[0], d["topk_idx"].shape[1], nsplit, head_groups, stream)
+    return mlasd.mla_sparse_decode(d["q"], d["kv_pages"], d["page_table"], d["topk_idx"], d["seq_lens"],
+                                   scale, out=out, lse=lse, stream=stream, nsplit=nsplit,
+                                   head_groups=head_groups)
 
 
 def check_attention(out, lse, ref_out, ref_lse, label=""):

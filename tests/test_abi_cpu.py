@@ -1,5 +1,5 @@
 """C-ABI checks that need no GPU: the library loads, exports every function
-include/mlasd.h declares, rejects bad arguments on the host before touching
+include/mlasd.h declares, rejects bad descriptors on the host before touching
 a device, and plans splits as documented."""
 import ctypes
 import os
@@ -11,6 +11,7 @@ import pytest
 import sparse_mla_decode_page_amd as m
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+U8, I32, BF16, F32 = 1, 2, 3, 4
 
 
 def _declared_functions():
@@ -26,8 +27,8 @@ def _declared_functions():
 def test_header_declares_entry_points():
     names = _declared_functions()
     for n in ("mla_sparse_decode", "mla_sparse_decode_ex", "mla_sparse_gather_dequant",
-              "mla_sparse_plan", "mla_kv_append", "mlasd_prepare", "mlasd_release",
-              "mlasd_workspace_bytes", "mlasd_status_string"):
+              "mla_sparse_plan", "mla_sparse_workspace_size", "mla_kv_append", "mlasd_prepare",
+              "mlasd_reserve", "mlasd_release", "mlasd_workspace_bytes", "mlasd_status_string"):
         assert n in names
 
 
@@ -41,76 +42,221 @@ def test_library_exports_every_declared_symbol():
         assert getattr(lib, n) is not None
 
 
+def test_descriptor_layout_matches_header():
+    """mlasd_tensor is pointer, two int32, then two int64[4]: 80 bytes."""
+    assert ctypes.sizeof(m.Tensor) == 8 + 4 + 4 + 32 + 32
+    assert m.Tensor.shape.offset == 16 and m.Tensor.stride.offset == 48
+
+
 def test_status_strings():
     lib = m.load_library()
-    for code in (0, -1, -2, -3, -4, -5, -6, -7):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert m.status_string(code) != "unknown status"
     assert m.status_string(-99) == "unknown status"
     assert lib.mlasd_version().decode().startswith("mlasd")
 
 
-def _decode(lib, q=0x1000, kv=0x1000, num_pages=1, pt=0x1000, max_pages=1, idx=0x1000, topk=4,
-            lens=0x1000, batch=1, scale=0.1, out=0x1000, lse=0x1000, nsplit=None, hg=0):
-    vp = ctypes.c_void_p
-    args = (vp(q), vp(kv), num_pages, vp(pt), max_pages, vp(idx), topk, vp(lens), batch, scale,
-            vp(out), vp(lse))
+def _t(data, dtype, shape, stride=None):
+    d = m.Tensor()
+    d.data = data
+    d.dtype = dtype
+    d.ndim = len(shape)
+    if stride is None:
+        stride, acc = [], 1
+        for s in reversed(shape):
+            stride.insert(0, acc)
+            acc *= s
+    for k, (s, st) in enumerate(zip(shape, stride)):
+        d.shape[k] = s
+        d.stride[k] = st
+    return d
+
+
+def _decode_args(B=2, topk=4, num_pages=3, max_pages=2):
+    """Descriptors of a well-formed decode call with fake (never touched) pointers."""
+    return dict(
+        q=_t(0x10000, BF16, [B, 64, 512]),
+        kv=_t(0x20000, U8, [num_pages, 149504]),
+        pt=_t(0x30000, I32, [B, max_pages]),
+        idx=_t(0x40000, I32, [B, topk]),
+        lens=_t(0x50000, I32, [B]),
+        out=_t(0x60000, BF16, [B, 64, 448]),
+        lse=_t(0x70000, F32, [B, 64]),
+    )
+
+
+def _decode(lib, a, scale=0.1, nsplit=None, hg=0):
+    r = ctypes.byref
+    args = (r(a["q"]), r(a["kv"]), r(a["pt"]), r(a["idx"]), r(a["lens"]), ctypes.c_float(scale),
+            r(a["out"]), r(a["lse"]))
     if nsplit is None:
-        return lib.mla_sparse_decode(*args, vp(0))
-    return lib.mla_sparse_decode_ex(*args, nsplit, hg, vp(0))
+        return lib.mla_sparse_decode(*args, None)
+    return lib.mla_sparse_decode_ex(*args, nsplit, hg, None)
 
 
-@pytest.mark.parametrize("kw,code", [
-    (dict(batch=-1), -2), (dict(topk=-1), -2), (dict(topk=513), -2), (dict(num_pages=0), -2),
-    (dict(max_pages=0), -2), (dict(kv=0), -1), (dict(pt=0), -1), (dict(lens=0), -1),
-    (dict(idx=0), -1), (dict(q=0), -1), (dict(out=0), -1), (dict(lse=0), -1),
-    (dict(q=0x1008), -3), (dict(kv=0x1004), -3), (dict(out=0x1004), -3), (dict(lse=0x1002), -3),
-    (dict(idx=0x1002), -3), (dict(scale=float("nan")), -4), (dict(scale=float("inf")), -4),
-    (dict(batch=0), 0), (dict(batch=0, q=0, out=0, lse=0), 0),
-    (dict(topk=600, nsplit=2), -2), (dict(nsplit=2, hg=3), -2), (dict(nsplit=2, hg=5), -2), (dict(nsplit=0, hg=-1), -2),
-])
-def test_host_validation_without_device(kw, code):
+def _mut(name, **kw):
+    def f(a):
+        d = a[name]
+        for k, v in kw.items():
+            if k in ("shape", "stride"):
+                for i, x in enumerate(v):
+                    getattr(d, k)[i] = x
+            else:
+                setattr(d, k, v)
+    return f
+
+
+CASES = [
+    ("q null", _mut("q", data=0), -1),
+    ("kv null", _mut("kv", data=0), -1),
+    ("out null", _mut("out", data=0), -1),
+    ("lse null", _mut("lse", data=0), -1),
+    ("q dtype", _mut("q", dtype=F32), -2),
+    ("q heads", _mut("q", shape=[2, 32, 512]), -2),
+    ("q dim", _mut("q", shape=[2, 64, 576]), -2),
+    ("q batch", _mut("q", shape=[3, 64, 512]), -2),
+    ("q inner stride", _mut("q", stride=[32768, 512, 2]), -2),
+    ("q misaligned", _mut("q", data=0x10008), -3),
+    ("q head stride not x8", _mut("q", stride=[64 * 516, 516, 1]), -3),
+    ("q batch stride padded ok-ish but not x8", _mut("q", stride=[32772, 512, 1]), -3),
+    ("kv row bytes", _mut("kv", shape=[3, 147456]), -2),
+    ("kv page stride < page", _mut("kv", stride=[147456, 1]), -2),
+    ("kv page stride not x16", _mut("kv", stride=[149512, 1]), -3),
+    ("kv misaligned", _mut("kv", data=0x20004), -3),
+    ("kv empty pool", _mut("kv", shape=[0, 149504]), -2),
+    ("pt batch", _mut("pt", shape=[3, 2]), -2),
+    ("pt zero pages", _mut("pt", shape=[2, 0]), -2),
+    ("pt dtype", _mut("pt", dtype=U8), -2),
+    ("idx topk > 512", _mut("idx", shape=[2, 513]), -2),
+    ("idx misaligned", _mut("idx", data=0x40002), -3),
+    ("lens rank", _mut("lens", ndim=2), -2),
+    ("out dims", _mut("out", shape=[2, 64, 512]), -2),
+    ("out misaligned", _mut("out", data=0x60008), -3),
+    ("lse shape", _mut("lse", shape=[2, 32]), -2),
+    ("lse misaligned", _mut("lse", data=0x70002), -3),
+    ("negative stride", _mut("pt", stride=[-2, 1]), -2),
+]
+
+
+@pytest.mark.parametrize("name,mutate,code", CASES, ids=[c[0] for c in CASES])
+def test_host_validation_without_device(name, mutate, code):
     lib = m.load_library()
-    assert _decode(lib, **kw) == code
+    a = _decode_args()
+    mutate(a)
+    assert _decode(lib, a) == code
+
+
+def test_scalar_and_plan_validation_without_device():
+    lib = m.load_library()
+    assert _decode(lib, _decode_args(), scale=float("nan")) == -4
+    assert _decode(lib, _decode_args(), scale=float("inf")) == -4
+    for hg in (3, 5, -1):
+        assert _decode(lib, _decode_args(), nsplit=2, hg=hg) == -2
+
+
+def test_empty_batch_is_a_noop_without_device():
+    lib = m.load_library()
+    a = _decode_args(B=0)
+    assert _decode(lib, a) == 0
+    for k in ("q", "out", "lse", "idx", "lens"):
+        a[k].data = 0
+    assert _decode(lib, a) == 0
+
+
+def test_strided_views_pass_host_validation():
+    """Padded page rows, a batch-strided q/out and a shared (stride 0) page
+    table are accepted by the host checks; the call then needs a device
+    (HIP error here, with no GPU), which proves validation went through."""
+    lib = m.load_library()
+    a = _decode_args()
+    a["kv"] = _t(0x20000, U8, [3, 149504], [149504 + 512, 1])
+    a["q"] = _t(0x10000, BF16, [2, 64, 512], [64 * 512 + 64, 512, 1])
+    a["out"] = _t(0x60000, BF16, [2, 64, 448], [64 * 512, 512, 1])
+    a["pt"] = _t(0x30000, I32, [2, 2], [0, 1])
+    a["lens"] = _t(0x50000, I32, [2], [3])
+    assert _decode(lib, a) in (-5, -6)
 
 
 def test_gather_hook_validation_without_device():
     lib = m.load_library()
-    vp = ctypes.c_void_p
+    r = ctypes.byref
+    a = _decode_args()
+    rows = _t(0x80000, F32, [2, 4, 512])
+    valid = _t(0x90000, U8, [2, 4])
     f = lib.mla_sparse_gather_dequant
-    assert f(vp(0x1000), 1, vp(0x1000), 1, vp(0x1000), 4, vp(0x1000), -1, vp(0x1000), vp(0x1000),
-             vp(0x1000), vp(0)) == -2
-    assert f(vp(0x1000), 1, vp(0x1000), 1, vp(0x1000), 4, vp(0x1000), 1, vp(0), vp(0x1000),
-             vp(0x1000), vp(0)) == -1
-    assert f(vp(0x1000), 1, vp(0x1000), 1, vp(0x1000), 4, vp(0x1000), 1, vp(0x1008), vp(0x1000),
-             vp(0x1000), vp(0)) == -3
-    assert f(vp(0x1000), 1, vp(0x1000), 1, vp(0x1000), 0, vp(0x1000), 1, vp(0), vp(0), vp(0), vp(0)) == 0
+    assert f(r(a["kv"]), r(a["pt"]), r(a["idx"]), r(a["lens"]), r(_t(0, F32, [2, 4, 512])), r(valid), None) == -1
+    assert f(r(a["kv"]), r(a["pt"]), r(a["idx"]), r(a["lens"]), r(_t(0x80000, BF16, [2, 4, 512])), r(valid),
+             None) == -2
+    assert f(r(a["kv"]), r(a["pt"]), r(a["idx"]), r(a["lens"]), r(_t(0x80008, F32, [2, 4, 512])), r(valid),
+             None) == -3
+    assert f(r(a["kv"]), r(a["pt"]), r(a["idx"]), r(a["lens"]), r(rows), r(_t(0x90000, U8, [2, 5])), None) == -2
+    e = _decode_args(topk=0)
+    assert f(r(e["kv"]), r(e["pt"]), r(e["idx"]), r(e["lens"]), r(_t(0, F32, [2, 0, 512])),
+             r(_t(0, U8, [2, 0])), None) == 0
 
 
 def test_prepare_validation_without_device():
     lib = m.load_library()
-    vp = ctypes.c_void_p
-    assert lib.mlasd_prepare(vp(0), -1, 512) == -2
-    assert lib.mlasd_prepare(vp(0), 4, 513) == -2
-    assert lib.mlasd_prepare(vp(0), 4, -1) == -2
-    assert lib.mlasd_workspace_bytes(vp(0), None) == -1
+    assert lib.mlasd_prepare(None, -1, 512) == -2
+    assert lib.mlasd_prepare(None, 4, 513) == -2
+    assert lib.mlasd_prepare(None, 4, -1) == -2
+    assert lib.mlasd_reserve(None, 0) == 0
+    assert lib.mlasd_workspace_bytes(None, None) == -1
 
 
-def _append(lib, latent=0x1000, seq=0x1000, pos=0x1000, n=4, pt=0x1000, batch=1, max_pages=1,
-            kv=0x1000, num_pages=1):
-    vp = ctypes.c_void_p
-    return lib.mla_kv_append(vp(latent), vp(seq), vp(pos), n, vp(pt), batch, max_pages, vp(kv),
-                             num_pages, vp(0))
+def test_workspace_size_host_only():
+    """Bytes of fp32 partials (448 values + 1 lse per head, slice and query)
+    for split plans, 0 for unsplit ones -- planned for a given CU count, so no
+    device is needed."""
+    assert m.workspace_size(16, 512, 4, 0, 256) == 16 * 4 * 64 * 449 * 4
+    assert m.workspace_size(256, 512, 0, 0, 256) == 0
+    ns = m.plan(1, 512, 0, 256)[0]
+    assert m.workspace_size(1, 512, 0, 0, 256) == ns * 64 * 449 * 4
+    with pytest.raises(m.MlasdError):
+        m.workspace_size(1, 513, 0, 0, 256)
+    with pytest.raises(m.MlasdError):
+        m.workspace_size(1, 512, 0, 3, 256)
 
 
-@pytest.mark.parametrize("kw,code", [
-    (dict(n=-1), -2), (dict(batch=-1), -2), (dict(batch=0), -2), (dict(max_pages=0), -2),
-    (dict(num_pages=0), -2), (dict(latent=0), -1), (dict(seq=0), -1), (dict(pos=0), -1),
-    (dict(pt=0), -1), (dict(kv=0), -1), (dict(latent=0x1008), -3), (dict(kv=0x1008), -3),
-    (dict(pos=0x1002), -3), (dict(n=0), 0), (dict(n=0, latent=0, kv=0), 0),
-])
-def test_append_validation_without_device(kw, code):
+def _append_args(n=4, B=2, max_pages=2, num_pages=3):
+    return dict(lat=_t(0x10000, BF16, [n, 512]), seq=_t(0x20000, I32, [n]), pos=_t(0x30000, I32, [n]),
+                pt=_t(0x40000, I32, [B, max_pages]), kv=_t(0x50000, U8, [num_pages, 149504]))
+
+
+def _append(lib, a):
+    r = ctypes.byref
+    return lib.mla_kv_append(r(a["lat"]), r(a["seq"]), r(a["pos"]), r(a["pt"]), r(a["kv"]), None)
+
+
+ACASES = [
+    ("latent null", _mut("lat", data=0), -1),
+    ("latent dims", _mut("lat", shape=[4, 448]), -2),
+    ("latent misaligned", _mut("lat", data=0x10008), -3),
+    ("latent row stride", _mut("lat", stride=[516, 1]), -3),
+    ("seq count", _mut("seq", shape=[3]), -2),
+    ("pos null", _mut("pos", data=0), -1),
+    ("pos misaligned", _mut("pos", data=0x30002), -3),
+    ("pt empty batch", _mut("pt", shape=[0, 2]), -2),
+    ("pt zero pages", _mut("pt", shape=[2, 0]), -2),
+    ("kv empty", _mut("kv", shape=[0, 149504]), -2),
+    ("kv misaligned", _mut("kv", data=0x50008), -3),
+]
+
+
+@pytest.mark.parametrize("name,mutate,code", ACASES, ids=[c[0] for c in ACASES])
+def test_append_validation_without_device(name, mutate, code):
     lib = m.load_library()
-    assert _append(lib, **kw) == code
+    a = _append_args()
+    mutate(a)
+    assert _append(lib, a) == code
+
+
+def test_append_zero_tokens_is_a_noop():
+    lib = m.load_library()
+    a = _append_args(n=0)
+    a["lat"].data = 0
+    a["kv"].data = 0
+    assert _append(lib, a) == 0
 
 
 @pytest.mark.parametrize("batch,topk,req,cus,expect", [

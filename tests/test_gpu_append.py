@@ -10,7 +10,7 @@ import sparse_mla_decode_page_amd as mlasd
 from gen import synth as G
 from oracle import mla_oracle as O
 
-from helpers import check_attention
+from helpers import check_attention, decode
 
 pytestmark = pytest.mark.gpu
 
@@ -177,10 +177,10 @@ def test_append_then_decode():
     scale = 1.0 / np.sqrt(192.0)
     ref_out, ref_lse = O.sparse_mla_decode(q, ref_pool, page_table, idx, lens, scale)
     dev = torch.device("cuda")
-    out, lse = mlasd.mla_sparse_decode(
-        torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).to(dev),
-        torch.from_numpy(got_pool).to(dev), torch.from_numpy(page_table).to(dev),
-        torch.from_numpy(idx).to(dev), torch.from_numpy(lens).to(dev), scale)
+    d = dict(q=torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).to(dev),
+             kv_pages=torch.from_numpy(got_pool).to(dev), page_table=torch.from_numpy(page_table).to(dev),
+             topk_idx=torch.from_numpy(idx).to(dev), seq_lens=torch.from_numpy(lens).to(dev))
+    out, lse = decode(d, scale)
     torch.cuda.synchronize()
     check_attention(out, lse, ref_out, ref_lse, label="decode after append")
 
@@ -241,3 +241,33 @@ def test_append_graph_capture_replay():
         g.replay()
         torch.cuda.synchronize()
         _assert_pool_equal(kv.cpu().numpy(), ref, f"graph replay {rep}")
+
+
+def test_append_strided_views():
+    """Latents as a row-strided view, ids and positions with strides, a
+    column-sliced page table and a pool at a padded page stride: the same
+    bytes as the oracle's append into a contiguous pool, and the padding
+    bytes untouched."""
+    rng = np.random.default_rng(91)
+    page_table = np.array([[2, 0], [1, -1]], dtype=np.int32)
+    seq = np.array([0] * 20 + [1] * 20, np.int32)
+    pos = np.concatenate([rng.choice(512, 20, replace=False), rng.choice(256, 20, replace=False)]).astype(np.int32)
+    bits = _group_mix(40, 92)
+    pool = _pool(3, 93)
+    ref = O.kv_append(pool, page_table, seq, pos, bits)
+    dev = torch.device("cuda")
+    wide = torch.full((3, PAGE + 256), 0xA5, dtype=torch.uint8, device=dev)
+    wide[:, :PAGE] = torch.from_numpy(pool).to(dev)
+    latbig = torch.zeros((40, 520), dtype=torch.bfloat16, device=dev)
+    latbig[:, 8:] = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    ids = torch.zeros((40, 2), dtype=torch.int32, device=dev)
+    ids[:, 1] = torch.from_numpy(seq).to(dev)
+    ps = torch.zeros((40, 3), dtype=torch.int32, device=dev)
+    ps[:, 2] = torch.from_numpy(pos).to(dev)
+    ptbig = torch.full((2, 5), 7, dtype=torch.int32, device=dev)
+    ptbig[:, 1:3] = torch.from_numpy(page_table).to(dev)
+    mlasd.mla_kv_append(latbig[:, 8:], ids[:, 1], ps[:, 2], ptbig[:, 1:3], wide[:, :PAGE])
+    torch.cuda.synchronize()
+    got = wide.cpu().numpy()
+    _assert_pool_equal(np.ascontiguousarray(got[:, :PAGE]), ref, "strided append")
+    assert np.all(got[:, PAGE:] == 0xA5)

@@ -13,7 +13,7 @@ import sparse_mla_decode_page_amd as mlasd
 from gen import synth as G
 from oracle import mla_oracle as O
 
-from helpers import check_attention, to_device
+from helpers import check_attention, decode, reserve_for, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -31,14 +31,9 @@ def config(i):
 
 def run(w, nsplit=None, stream=None):
     d = to_device(w)
-    out, lse = mlasd.mla_sparse_decode(d["q"], d["kv_pages"], d["page_table"], d["topk_idx"],
-                                       d["seq_lens"], w.softmax_scale, nsplit=nsplit, stream=stream)
+    out, lse = decode(d, w.softmax_scale, nsplit=nsplit, stream=stream)
     torch.cuda.synchronize()
     return out, lse
-
-
-def _bf16_to_f64(t):
-    return t.float().cpu().double().numpy()
 
 
 # ----------------------------------------------------------------------------
@@ -50,15 +45,13 @@ def test_gather_dequant_bit_exact(i):
     w, _ = config(i)
     print(f"gather config {i}", flush=True)
     d = to_device(w)
-    k, v, valid = mlasd.mla_sparse_gather_dequant(d["kv_pages"], d["page_table"], d["topk_idx"],
-                                                  d["seq_lens"])
+    got, valid = mlasd.mla_sparse_gather_dequant(d["kv_pages"], d["page_table"], d["topk_idx"],
+                                                 d["seq_lens"])
     torch.cuda.synchronize()
     rows, ok = O.gather_dequant(w.kv_pages, w.page_table, w.topk_idx, w.seq_lens)
     assert np.array_equal(valid.cpu().numpy().astype(bool), ok)
-    kk = _bf16_to_f64(k)
-    vv = v.float().cpu().double().numpy()
-    assert np.array_equal(kk, rows), np.argwhere(kk != rows)[:5]
-    assert np.array_equal(vv, rows[..., :448]), np.argwhere(vv != rows[..., :448])[:5]
+    gg = got.cpu().double().numpy()
+    assert np.array_equal(gg, rows), np.argwhere(gg != rows)[:5]
 
 
 def _all_codes_pool():
@@ -91,24 +84,21 @@ def test_gather_dequant_all_codes_all_scales():
     idx = np.arange(510, dtype=np.int32)[None][:, ::-1].copy()
     lens = np.array([510], dtype=np.int32)
     dev = lambda a: torch.from_numpy(a).cuda()
-    k, v, valid = mlasd.mla_sparse_gather_dequant(dev(pool), dev(pt), dev(idx), dev(lens))
+    got, valid = mlasd.mla_sparse_gather_dequant(dev(pool), dev(pt), dev(idx), dev(lens))
     torch.cuda.synchronize()
     rows, ok = O.gather_dequant(pool, pt, idx, lens)
     assert ok.all() and valid.cpu().numpy().all()
     with np.errstate(over="ignore"):
         r32 = torch.from_numpy(rows.astype(np.float32))
-    exp_v = r32[..., :448].to(torch.float16).double().numpy()
-    exp_k = np.concatenate([exp_v, r32[..., 448:].to(torch.bfloat16).double().numpy()], axis=-1)
-    kk = _bf16_to_f64(k)
-    vv = v.float().cpu().double().numpy()
-    for got, want in ((kk, exp_k), (vv, exp_v)):
-        nan = np.isnan(want)
-        assert np.array_equal(np.isnan(got), nan)
-        bad = np.argwhere(got[~nan] != want[~nan])
-        assert len(bad) == 0, (len(bad), got[~nan][bad[:5, 0]], want[~nan][bad[:5, 0]])
+    exp = np.concatenate([r32[..., :448].to(torch.float16).double().numpy(), rows[..., 448:]], axis=-1)
+    gg = got.cpu().double().numpy()
+    nan = np.isnan(exp)
+    assert np.array_equal(np.isnan(gg), nan)
+    bad = np.argwhere(gg[~nan] != exp[~nan])
+    assert len(bad) == 0, (len(bad), gg[~nan][bad[:5, 0]], exp[~nan][bad[:5, 0]])
     # and exactly the oracle's values wherever those are representable
-    same = exp_k == rows
-    assert np.array_equal(kk[same], rows[same])
+    same = exp == rows
+    assert np.array_equal(gg[same], rows[same])
 
 
 # ----------------------------------------------------------------------------
@@ -140,8 +130,7 @@ def test_head_groups_bitwise_equal(i, nsplit):
     w, (ref_out, ref_lse) = config(i)
     print(f"head groups config {i} nsplit={nsplit}", flush=True)
     d = to_device(w)
-    r = [mlasd.mla_sparse_decode(d["q"], d["kv_pages"], d["page_table"], d["topk_idx"], d["seq_lens"],
-                                 w.softmax_scale, nsplit=nsplit, head_groups=hg) for hg in (1, 2, 4)]
+    r = [decode(d, w.softmax_scale, nsplit=nsplit, head_groups=hg) for hg in (1, 2, 4)]
     torch.cuda.synchronize()
     for o, l in r[1:]:
         assert torch.equal(r[0][0], o) and torch.equal(r[0][1], l)
@@ -215,8 +204,8 @@ def test_topk_zero_and_batch_zero():
     assert np.all(out.float().cpu().numpy() == 0) and np.all(np.isneginf(lse.cpu().numpy()))
     d = to_device(_custom(4, [500], 8))
     e = {k: v[:0] for k, v in d.items() if k != "kv_pages"}
-    out, lse = mlasd.mla_sparse_decode(e["q"], d["kv_pages"], e["page_table"], e["topk_idx"],
-                                       e["seq_lens"], 0.1)
+    e["kv_pages"] = d["kv_pages"]
+    out, lse = decode(e, 0.1)
     assert out.shape == (0, 64, 448) and lse.shape == (0, 64)
 
 
@@ -279,8 +268,7 @@ def test_repeat_calls_deterministic():
     d = to_device(w)
     outs = []
     for _ in range(3):
-        o, l = mlasd.mla_sparse_decode(d["q"], d["kv_pages"], d["page_table"], d["topk_idx"],
-                                       d["seq_lens"], w.softmax_scale)
+        o, l = decode(d, w.softmax_scale)
         outs.append((o.clone(), l.clone()))
     torch.cuda.synchronize()
     for o, l in outs[1:]:
@@ -299,15 +287,13 @@ def test_graph_capture_replay():
     with torch.cuda.stream(side):
         for w, d in zip(ws, devs):
             for ns in (None, 1):
-                o, l = mlasd.mla_sparse_decode(d["q"], d["kv_pages"], d["page_table"], d["topk_idx"],
-                                               d["seq_lens"], w.softmax_scale, nsplit=ns, stream=side)
+                o, l = decode(d, w.softmax_scale, nsplit=ns, stream=side)
                 outs.append((o, l, o.clone(), l.clone(), w, d, ns))
     side.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=side):
         for o, l, _, _, w, d, ns in outs:
-            mlasd.mla_sparse_decode(d["q"], d["kv_pages"], d["page_table"], d["topk_idx"],
-                                    d["seq_lens"], w.softmax_scale, out=o, lse=l, nsplit=ns, stream=side)
+            decode(d, w.softmax_scale, nsplit=ns, stream=side, out=o, lse=l, reserve=False)
     for rep in range(3):
         for o, l, _, _, _, _, _ in outs:
             o.zero_()
@@ -319,8 +305,7 @@ def test_graph_capture_replay():
             assert torch.equal(o, o_ref) and torch.equal(l, l_ref), f"replay {rep} nsplit={ns}"
         # eager work between replays
         w, d = ws[0], devs[0]
-        mlasd.mla_sparse_decode(d["q"], d["kv_pages"], d["page_table"], d["topk_idx"], d["seq_lens"],
-                                w.softmax_scale)
+        decode(d, w.softmax_scale)
         torch.cuda.synchronize()
 
 
@@ -336,15 +321,13 @@ def test_graph_replay_timed_workload():
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        o_eager, l_eager = mlasd.mla_sparse_decode(d["q"], d["kv_pages"], d["page_table"], d["topk_idx"],
-                                                   d["seq_lens"], w.softmax_scale, stream=side)
+        o_eager, l_eager = decode(d, w.softmax_scale, stream=side)
     side.synchronize()
     o = torch.empty_like(o_eager)
     l = torch.empty_like(l_eager)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=side):
-        mlasd.mla_sparse_decode(d["q"], d["kv_pages"], d["page_table"], d["topk_idx"], d["seq_lens"],
-                                w.softmax_scale, out=o, lse=l, stream=side)
+        decode(d, w.softmax_scale, stream=side, out=o, lse=l, reserve=False)
     for rep in range(3):
         o.zero_()
         l.zero_()
@@ -355,32 +338,44 @@ def test_graph_replay_timed_workload():
     check_attention(o, l, ref_out, ref_lse, label="config 3 graph replay")
 
 
-def test_prepare_capture_release():
-    """mlasd_prepare reserves a stream's split scratch, so a first split call
-    made under graph capture allocates nothing; without it the growth is
-    refused before anything is enqueued; mlasd_release frees the scratch."""
-    w, (ref_out, ref_lse) = config(2)   # B=16, topk=512: planned split (4 slices x 4 head groups)
+def _status(fn):
+    try:
+        fn()
+    except mlasd.MlasdError as e:
+        return e.status
+    return 0
+
+
+def test_split_scratch_discipline():
+    """The decode never allocates: a split call on a stream with no reserved
+    scratch returns MLASD_ERR_WORKSPACE (outside capture too) and writes
+    nothing; mlasd_prepare is the only allocator; a prepared capture replays
+    to the oracle; mlasd_release frees."""
+    w, (ref_out, ref_lse) = config(2)   # B=16, topk=512: a planned split
     assert mlasd.plan(w.batch, w.topk)[0] > 1
     d = to_device(w)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
-    out = torch.empty((w.batch, 64, 448), dtype=torch.bfloat16, device="cuda")
-    lse = torch.empty((w.batch, 64), dtype=torch.float32, device="cuda")
+    out = torch.full((w.batch, 64, 448), 7.0, dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((w.batch, 64), 7.0, dtype=torch.float32, device="cuda")
     assert mlasd.workspace_bytes(stream=s) == 0
+    call = lambda: decode(d, w.softmax_scale, stream=s, out=out, lse=lse, reserve=False)
+    assert _status(call) == mlasd._binding.STATUS_WORKSPACE
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all()) and bool((lse == 7.0).all()), "a refused call wrote output"
+    # nor does it allocate under capture
     g0 = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g0, stream=s):
         out.zero_()
-        with pytest.raises(mlasd.MlasdError, match="capturing"):
-            mlasd.mla_sparse_decode(d["q"], d["kv_pages"], d["page_table"], d["topk_idx"],
-                                    d["seq_lens"], w.softmax_scale, out=out, lse=lse, stream=s)
+        assert _status(call) == mlasd._binding.STATUS_WORKSPACE
     del g0
+    assert mlasd.workspace_bytes(stream=s) == 0
     mlasd.prepare(w.batch, w.topk, stream=s)
     ns = mlasd.plan(w.batch, w.topk)[0]
     assert mlasd.workspace_bytes(stream=s) >= w.batch * ns * 64 * 449 * 4
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
-        mlasd.mla_sparse_decode(d["q"], d["kv_pages"], d["page_table"], d["topk_idx"],
-                                d["seq_lens"], w.softmax_scale, out=out, lse=lse, stream=s)
+        call()
     for rep in range(2):
         out.zero_()
         lse.zero_()
@@ -394,12 +389,77 @@ def test_prepare_capture_release():
     mlasd.release(stream=s)   # nothing held: no-op
 
 
+def test_graph_survives_scratch_growth():
+    """A graph captured with the stream's scratch keeps working after a
+    larger reservation on that stream replaced the buffer and a larger eager
+    split call ran there: the superseded buffer stays allocated until
+    mlasd_release, so the replay neither reads freed memory nor races the
+    new buffer."""
+    w_small, ref_small = config(1)       # B=1: planned split
+    w_big, ref_big = config(2)           # B=16: planned split, larger scratch
+    ds, db = to_device(w_small), to_device(w_big)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    mlasd.prepare(1, 512, stream=s)
+    before = mlasd.workspace_bytes(stream=s)
+    o = torch.empty((1, 64, 448), dtype=torch.bfloat16, device="cuda")
+    l = torch.empty((1, 64), dtype=torch.float32, device="cuda")
+    with torch.cuda.stream(s):
+        o_eager, l_eager = decode(ds, w_small.softmax_scale, stream=s, reserve=False)
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        decode(ds, w_small.softmax_scale, stream=s, out=o, lse=l, reserve=False)
+    mlasd.prepare(w_big.batch, 512, stream=s)          # grows: the old buffer is kept
+    assert mlasd.workspace_bytes(stream=s) > before
+    for rep in range(3):
+        o.zero_()
+        l.zero_()
+        with torch.cuda.stream(s):
+            ob, lb = decode(db, w_big.softmax_scale, stream=s, reserve=False)   # uses the new buffer
+            g.replay()                                                          # uses the old one
+        s.synchronize()
+        assert torch.equal(o, o_eager) and torch.equal(l, l_eager), f"replay {rep}"
+        check_attention(ob, lb, ref_big[0], ref_big[1], label=f"larger eager call {rep}")
+    del g
+    mlasd.release(stream=s)
+
+
+def test_strided_views_match_contiguous():
+    """Pages at a padded row stride (a [:, :149504] view of a wider pool, as
+    the pages' own harness builds), q and out as views into larger buffers,
+    a page table that is a column slice and strided seq_lens give bit for
+    bit the contiguous call's results."""
+    w, (ref_out, ref_lse) = config(2)
+    d = to_device(w)
+    o_ref, l_ref = decode(d, w.softmax_scale)
+    B, P = w.batch, w.num_pages
+    wide = torch.zeros((P, 149504 + 4096), dtype=torch.uint8, device="cuda")
+    wide[:, :149504] = d["kv_pages"]
+    qbig = torch.zeros((B, 66, 520), dtype=torch.bfloat16, device="cuda")
+    qbig[:, 1:65, 8:520] = d["q"]
+    ptbig = torch.full((B, w.max_pages + 3), -5, dtype=torch.int32, device="cuda")
+    ptbig[:, 2:2 + w.max_pages] = d["page_table"]
+    lbig = torch.zeros((B, 3), dtype=torch.int32, device="cuda")
+    lbig[:, 1] = d["seq_lens"]
+    obig = torch.full((B, 65, 456), 3.0, dtype=torch.bfloat16, device="cuda")
+    lsebig = torch.full((B, 70), 3.0, dtype=torch.float32, device="cuda")
+    v = dict(q=qbig[:, 1:65, 8:520], kv_pages=wide[:, :149504], page_table=ptbig[:, 2:2 + w.max_pages],
+             topk_idx=d["topk_idx"], seq_lens=lbig[:, 1])
+    assert not v["kv_pages"].is_contiguous() and not v["q"].is_contiguous()
+    o, l = decode(v, w.softmax_scale, out=obig[:, :64, 8:456], lse=lsebig[:, 3:67])
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(l, l_ref)
+    assert bool((obig[:, 64] == 3.0).all()) and bool((obig[:, :, :8] == 3.0).all())
+    assert bool((lsebig[:, :3] == 3.0).all()) and bool((lsebig[:, 67:] == 3.0).all())
+
+
 def test_split_merge_alternating_inputs():
-    """The fused LSE merge reads partials written by other workgroups of the
-    same launch: alternate two input sets of one shape on one stream, with no
-    host synchronisation between launches, and check every result against
-    the first result of its set (bitwise) and against the oracle.  A merge
-    that read a stale partial of the previous launch would differ."""
+    """The LSE combine reads partials the decode launch just wrote to the
+    stream's scratch: alternate two input sets of one shape on one stream,
+    with no host synchronisation between launches, and check every result
+    against the first result of its set (bitwise) and against the oracle.  A
+    combine that read partials of the previous launch would differ."""
     base = config(3)[0]
     # rotation_sets writes records into the pool: work on a copy
     w, w2 = G.rotation_sets(dataclasses.replace(base, kv_pages=base.kv_pages.copy()), 2, seed=4242)
@@ -409,11 +469,11 @@ def test_split_merge_alternating_inputs():
                                w2.softmax_scale)
     d1, d2 = to_device(w), to_device(w2)
     for ns in (4, 16):
+        reserve_for(w.batch, w.topk, ns)
         res = []
         for it in range(8):
             d = d1 if it % 2 == 0 else d2
-            o, l = mlasd.mla_sparse_decode(d["q"], d["kv_pages"], d["page_table"], d["topk_idx"],
-                                           d["seq_lens"], w.softmax_scale, nsplit=ns)
+            o, l = decode(d, w.softmax_scale, nsplit=ns, reserve=False)
             res.append((o, l))
         torch.cuda.synchronize()
         for it, (o, l) in enumerate(res):
@@ -421,7 +481,7 @@ def test_split_merge_alternating_inputs():
             assert torch.equal(o, o0) and torch.equal(l, l0), f"nsplit={ns} launch {it}"
         check_attention(res[0][0], res[0][1], ref_out, ref_lse, label=f"set A nsplit={ns}")
         check_attention(res[1][0], res[1][1], ref2[0], ref2[1], label=f"set B nsplit={ns}")
-    # the arrival counters are back at zero: a smaller batch on the same stream
+    # a smaller batch on the same stream afterwards
     ws = G.make_config(2)
     ref_s = O.sparse_mla_decode(ws.q_bits, ws.kv_pages, ws.page_table, ws.topk_idx, ws.seq_lens,
                                 ws.softmax_scale)
@@ -459,8 +519,7 @@ def test_validation_matrix(batch, topk):
                                            w.seq_lens, w.softmax_scale)
     d = to_device(w)
     for ns, hg in ((None, None), (1, 1), (1, 2), (1, 4)):
-        out, lse = mlasd.mla_sparse_decode(d["q"], d["kv_pages"], d["page_table"], d["topk_idx"],
-                                           d["seq_lens"], w.softmax_scale, nsplit=ns, head_groups=hg)
+        out, lse = decode(d, w.softmax_scale, nsplit=ns, head_groups=hg)
         torch.cuda.synchronize()
         check_attention(out, lse, ref_out, ref_lse,
                         label=f"B={batch:2d} H=64 topk={topk} nsplit={ns or 'plan'} "
