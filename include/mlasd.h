@@ -156,6 +156,28 @@ int mla_sparse_decode_ex(const mlasd_tensor* q, const mlasd_tensor* kv_pages,
                          int32_t nsplit, int32_t head_groups, mlasd_stream_t stream);
 
 /*
+ * mla_sparse_decode_noalloc -- mla_sparse_decode for callers that cannot
+ * allocate device memory at all: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments, plan and
+ * results as mla_sparse_decode (bit for bit).  It needs no mlasd_prepare:
+ * split partials go to a static device array of 16 MiB per GPU, held by
+ * the library until the process ends; a call whose plan needs more
+ * (B * nsplit * 64 * 449 * 4 bytes > 16 MiB; no automatic plan up to
+ * B = 56 at top-k 512 on 256 CUs does) returns MLASD_ERR_WORKSPACE and
+ * enqueues nothing.  It calls no hipMalloc, hipFree or other allocating
+ * routine.  Every call on one GPU shares that GPU's array: calls that may
+ * overlap in time on one GPU (different streams without ordering, or
+ * replays of graphs containing this call) race on it and must be ordered
+ * by the caller.  The array keeps the last call's partials; nothing in it
+ * needs to start at zero.
+ */
+int mla_sparse_decode_noalloc(const mlasd_tensor* q, const mlasd_tensor* kv_pages,
+                              const mlasd_tensor* page_table, const mlasd_tensor* topk_idx,
+                              const mlasd_tensor* seq_lens, float softmax_scale,
+                              const mlasd_tensor* out, const mlasd_tensor* lse,
+                              mlasd_stream_t stream);
+
+/*
  * mla_sparse_plan -- the plan the library would use (host only, no device
  * work): writes the number of top-k slices per query, the number of index
  * entries per slice (a multiple of 32) and, if head_groups is not NULL, the

@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     load_library,
     mla_kv_append,
     mla_sparse_decode,
+    mla_sparse_decode_noalloc,
     mla_sparse_gather_dequant,
     plan,
     prepare,
@@ -21,6 +22,6 @@ from ._binding import (  # noqa: F401
     workspace_size,
 )
 
-__all__ = ["mla_sparse_decode", "mla_sparse_gather_dequant", "mla_kv_append", "plan", "prepare",
+__all__ = ["mla_sparse_decode", "mla_sparse_decode_noalloc", "mla_sparse_gather_dequant", "mla_kv_append", "plan", "prepare",
            "reserve", "release", "workspace_bytes", "workspace_size", "describe", "Tensor",
            "load_library", "library_path", "status_string", "MlasdError"]

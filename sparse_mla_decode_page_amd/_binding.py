@@ -58,6 +58,7 @@ def load_library():
     T = ctypes.POINTER(Tensor)
     lib.mla_sparse_decode.argtypes = [T, T, T, T, T, f32, T, T, vp]
     lib.mla_sparse_decode_ex.argtypes = [T, T, T, T, T, f32, T, T, i32, i32, vp]
+    lib.mla_sparse_decode_noalloc.argtypes = [T, T, T, T, T, f32, T, T, vp]
     lib.mla_sparse_plan.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                     ctypes.POINTER(i32)]
     lib.mla_sparse_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
@@ -67,7 +68,7 @@ def load_library():
     lib.mlasd_reserve.argtypes = [vp, sz]
     lib.mlasd_release.argtypes = [vp]
     lib.mlasd_workspace_bytes.argtypes = [vp, ctypes.POINTER(sz)]
-    for name in ("mla_sparse_decode", "mla_sparse_decode_ex", "mla_sparse_plan",
+    for name in ("mla_sparse_decode", "mla_sparse_decode_ex", "mla_sparse_decode_noalloc", "mla_sparse_plan",
                  "mla_sparse_workspace_size", "mla_sparse_gather_dequant", "mla_kv_append",
                  "mlasd_prepare", "mlasd_reserve", "mlasd_release", "mlasd_workspace_bytes"):
         getattr(lib, name).restype = ctypes.c_int
@@ -217,6 +218,22 @@ def mla_sparse_decode(q, kv_pages, page_table, topk_idx, seq_lens, softmax_scale
             rc = lib.mla_sparse_decode_ex(*args, int(nsplit or 0), int(head_groups or 0),
                                           _stream(stream, dev))
     _check(rc, "mla_sparse_decode")
+    return out, lse
+
+
+def mla_sparse_decode_noalloc(q, kv_pages, page_table, topk_idx, seq_lens, softmax_scale, out, lse,
+                              stream=None):
+    """mla_sparse_decode through the entry point that allocates nothing (its
+    split partials live in the library's static per-GPU array).  `out` and
+    `lse` must be given: this path allocates no tensors either."""
+    dev = _same_device(q, kv_pages, page_table, topk_idx, seq_lens, out, lse)
+    lib = load_library()
+    descs = [describe(t) for t in (q, kv_pages, page_table, topk_idx, seq_lens)]
+    do, dl = describe(out), describe(lse)
+    with torch.cuda.device(dev):
+        args = [ctypes.byref(d) for d in descs] + [float(softmax_scale), ctypes.byref(do), ctypes.byref(dl)]
+        rc = lib.mla_sparse_decode_noalloc(*args, _stream(stream, dev))
+    _check(rc, "mla_sparse_decode_noalloc")
     return out, lse
 
 

@@ -395,6 +395,26 @@ int mla_sparse_decode_ex(const mlasd_tensor* q, const mlasd_tensor* kv_pages, co
                      head_groups, (hipStream_t)stream);
 }
 
+int mla_sparse_decode_noalloc(const mlasd_tensor* q, const mlasd_tensor* kv_pages,
+                              const mlasd_tensor* page_table, const mlasd_tensor* topk_idx,
+                              const mlasd_tensor* seq_lens, float softmax_scale, const mlasd_tensor* out,
+                              const mlasd_tensor* lse, mlasd_stream_t stream) {
+  DecodeCall call;
+  int rc = prepare_decode(q, kv_pages, page_table, topk_idx, seq_lens, softmax_scale, out, lse, 0, 0, &call);
+  if (rc != MLASD_OK || call.p.batch == 0) return rc;
+  void* ws = nullptr;
+  if (call.p.nsplit > 1) {
+    int dev = 0;
+    rc = current_device(&dev);
+    if (rc != MLASD_OK) return rc;
+    if (dev >= mlasd::kMaxDevices) return MLASD_ERR_DEVICE;
+    if (split_scratch_bytes(call.p.batch, call.p.nsplit) > mlasd::kNoAllocScratchBytes) return MLASD_ERR_WORKSPACE;
+    hipError_t e = mlasd::noalloc_scratch(dev, &ws);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return launch_decode_call(call, ws, mlasd::kNoAllocScratchBytes, (hipStream_t)stream);
+}
+
 int mla_sparse_plan(int32_t batch, int32_t topk, int32_t nsplit_request, int32_t num_cus,
                     int32_t* nsplit, int32_t* split_len, int32_t* head_groups) {
   if (!nsplit || !split_len) return MLASD_ERR_NULL;

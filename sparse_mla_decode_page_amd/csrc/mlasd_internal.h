@@ -89,6 +89,13 @@ struct AppendParams {
   int64_t page_stride;
 };
 
+// Split scratch of the entry point that allocates nothing: a static device
+// array per GPU (mlasd_noalloc.hip).  noalloc_scratch returns its device
+// address on device `dev`, which must be current.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+constexpr int kMaxDevices = 64;
+hipError_t noalloc_scratch(int dev, void** ptr);
+
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_combine(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_gather(const GatherParams& p, hipStream_t stream);
