@@ -268,17 +268,22 @@ class Workbench:
         with torch.cuda.graph(g, stream=side):
             for i in range(steps):
                 self.step(i, side)
-        # untimed warm-up: at least --warmup steps and WARMUP_FLOOR_S of GPU work
-        warm = 0
-        t_warm = 0.0
+        # untimed warm-up, enqueued back to back so the clocks settle: at
+        # least --warmup steps and WARMUP_FLOOR_S of GPU work
         with torch.cuda.stream(side):
-            while warm < warmup or t_warm < WARMUP_FLOOR_S:
-                ev0.record(side)
+            ev0.record(side)
+            g.replay()
+            ev1.record(side)
+            ev1.synchronize()
+            t_one = ev0.elapsed_time(ev1) / 1e3
+            reps = max(math.ceil(max(warmup - steps, 0) / steps), math.ceil((WARMUP_FLOOR_S - t_one) / t_one), 0)
+            ev0.record(side)
+            for _ in range(reps):
                 g.replay()
-                ev1.record(side)
-                ev1.synchronize()
-                t_warm += ev0.elapsed_time(ev1) / 1e3
-                warm += steps
+            ev1.record(side)
+            ev1.synchronize()
+            warm = steps * (reps + 1)
+            t_warm = t_one + ev0.elapsed_time(ev1) / 1e3
             torch.cuda.synchronize()
             ev0.record(side)
             g.replay()
