@@ -45,7 +45,7 @@ APPEND_BYTES_PER_TOKEN = 512 * 2 + 4 + 4 + TOKEN_BYTES   # latent + seq id + pos
 WARMUP_FLOOR_S = 0.05           # untimed GPU work before timing, whatever --warmup says
 HEADLINE = 4
 METRIC = "sparse-MLA decode: attended (query·head·token)/s + achieved HBM GB/s vs peak"
-KERNEL_SOURCES = ["sparse_mla_decode_page_amd/csrc/mlasd_kernels.hip"]
+KERNEL_SOURCES = ["sparse_mla_decode_page_amd/csrc/mlasd_decode.hip", "sparse_mla_decode_page_amd/csrc/mlasd_combine.hip"]
 
 
 def log(*a):
@@ -207,7 +207,7 @@ class Workbench:
     """One workload on the device: rotating input sets, the step function,
     and the graph of exactly `steps` steps."""
 
-    def __init__(self, w, dev, nsplit, name):
+    def __init__(self, w, dev, nsplit, name, head_groups=0):
         import torch
         import sparse_mla_decode_page_amd as mlasd
         from gen.synth import rotation_sets
@@ -229,16 +229,22 @@ class Workbench:
                 out=torch.empty((w.batch, 64, 448), dtype=torch.bfloat16, device=dev),
                 lse=torch.empty((w.batch, 64), dtype=torch.float32, device=dev)))
         self.nsplit_arg = nsplit if nsplit > 0 else None
-        self.plan = mlasd.plan(w.batch, w.topk, nsplit)
+        self.hg_arg = head_groups if head_groups > 0 else None
+        ns, sl, hg = mlasd.plan(w.batch, w.topk, nsplit)
+        if head_groups > 0:   # the plan with the head groups forced
+            sl = max(32, -(-w.topk // max(1, nsplit or ns)) // 32 * 32 if nsplit else sl)
+            hg = head_groups
+        self.plan = (ns, sl, hg)
         self.stream = torch.cuda.Stream(dev)
-        mlasd.reserve(mlasd.workspace_size(w.batch, w.topk, nsplit), stream=self.stream)
+        mlasd.reserve(mlasd.workspace_size(w.batch, w.topk, nsplit, head_groups), stream=self.stream)
         log(f"{name}: {self.n_sets} input sets ready in {time.perf_counter() - t0:.1f} s, "
             f"plan (nsplit, split_len, head_groups) = {self.plan}")
 
     def step(self, i, stream):
         d = self.dsets[i % self.n_sets]
         self.mlasd.mla_sparse_decode(d["q"], self.kv, self.pt, d["idx"], self.lens, self.w.softmax_scale,
-                                     out=d["out"], lse=d["lse"], stream=stream, nsplit=self.nsplit_arg)
+                                     out=d["out"], lse=d["lse"], stream=stream, nsplit=self.nsplit_arg,
+                                     head_groups=self.hg_arg)
 
     def run(self, steps, warmup, graph=True):
         torch = self.torch
@@ -383,6 +389,7 @@ def main():
     ap.add_argument("--topk", type=int, default=512, help="custom workload: top-k width")
     ap.add_argument("--seq-len", type=int, default=65536, help="custom workload: tokens per sequence")
     ap.add_argument("--nsplit", type=int, default=0, help="force top-k slices per query (0 = plan)")
+    ap.add_argument("--head-groups", type=int, default=0, help="force workgroups per slice's heads (0 = plan)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager calls (counter-collection runs)")
@@ -452,7 +459,7 @@ def main():
         t0 = time.perf_counter()
         w = build()
         log(f"{key}: workload built in {time.perf_counter() - t0:.1f} s")
-        wb = Workbench(w, dev, args.nsplit, key)
+        wb = Workbench(w, dev, args.nsplit, key, args.head_groups)
         r = wb.run(args.steps, args.warmup, graph=not args.no_graph)
         s = wb.summary(r, key)
         s["workload"] = name

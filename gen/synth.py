@@ -158,11 +158,15 @@ def _write_records(pool: np.ndarray, pages, slots, codes, scale_bytes, rope_bits
     flat[sbase[:, None] + np.arange(SCALE_BYTES)] = srec
 
 
-def draw_records(rng, n, outlier_channels=None, outlier_sigma=20.0):
-    """Draw n token records: returns (codes [n,448], scale bytes [n,7], rope bf16 bits [n,64])."""
+def draw_records(rng, n, outlier_channels=None, outlier_sigma=20.0, group_scale=None):
+    """Draw n token records: returns (codes [n,448], scale bytes [n,7], rope bf16 bits [n,64]).
+    group_scale(rng, n) -> [n, 7] multiplies each 64-dim nope group (wide
+    dynamic-range caches)."""
     x = rng.standard_normal((n, D_NOPE))
     if outlier_channels is not None and len(outlier_channels):
         x[:, outlier_channels] *= outlier_sigma
+    if group_scale is not None:
+        x *= np.repeat(np.asarray(group_scale(rng, n), dtype=np.float64), GROUP, axis=1)
     rope = rng.standard_normal((n, D_ROPE))
     codes, sb = quantize_nope(x)
     return codes, sb, bf16_bits(rope)
@@ -170,7 +174,8 @@ def draw_records(rng, n, outlier_channels=None, outlier_sigma=20.0):
 
 def build_workload(seed, seq_lens, topk, *, name="custom", num_pages=None, max_pages=None,
                    outlier_frac=0.0, outlier_channels=None, fill="selected",
-                   index_order="random", softmax_scale=None, pool=None, page_table=None):
+                   index_order="random", softmax_scale=None, pool=None, page_table=None,
+                   group_scale=None):
     """General seeded builder.
 
     seq_lens    : per-query context lengths (>= 0)
@@ -182,6 +187,8 @@ def build_workload(seed, seq_lens, topk, *, name="custom", num_pages=None, max_p
     index_order : "random" (positions shuffled) or "sorted"
     pool, page_table : reuse an existing pool/page table (new index set on the
                   same cache); selected records are (re)drawn and written.
+    group_scale : optional callable (rng, n) -> [n, 7] multipliers of each
+                  record's nope groups before quantisation
     """
     rng = _rng(seed)
     seq_lens = np.asarray(seq_lens, dtype=np.int64)
@@ -237,7 +244,7 @@ def build_workload(seed, seq_lens, topk, *, name="custom", num_pages=None, max_p
         pg = page_table[bb, pos // PAGE_TOKENS].astype(np.int64)
         sl = pos % PAGE_TOKENS
     if len(pg):
-        codes, sb, rope = draw_records(rng, len(pg), outliers)
+        codes, sb, rope = draw_records(rng, len(pg), outliers, group_scale=group_scale)
         _write_records(pool, pg, sl, codes, sb, rope)
 
     scale = 1.0 / math.sqrt(D_QK) if softmax_scale is None else float(softmax_scale)

@@ -123,8 +123,13 @@ typedef struct mlasd_tensor {
  * allocates, frees or synchronises, so it may be captured into a graph.
  * Numerics: the 448 nope dims of q and K, and the value rows, enter the
  * contractions in fp16; the 64 rope dims in bf16; sums and the softmax are
- * fp32.  Dequantised cache values are exact in fp16 for UE8M0 bytes
- * 112..134; q's nope values for magnitudes in [2^-14, 65504].
+ * fp32.  Cache values stay exact over the UE8M0 range: a token whose 7
+ * group scales all lie in bytes 112..134 is held in fp16 as stored; any
+ * other token is held as e4m3 * 2^(k_g - r) with one power of two r per
+ * token (exact whenever its groups span at most 22 binades), which the
+ * score and P V take back in fp32.  Each head's q is scaled by a power of
+ * two that puts its largest nope value in [2^15, 2^16), so q is exact down
+ * to 2^29 below that value; the softmax scale takes the power back.
  * Returns MLASD_OK or a negative MLASD_ERR_* code.
  */
 int mla_sparse_decode(const mlasd_tensor* q, const mlasd_tensor* kv_pages,
@@ -140,10 +145,10 @@ int mla_sparse_decode(const mlasd_tensor* q, const mlasd_tensor* kv_pages,
  *                combine ("The Turning Point", Step 5).  <= 0: automatic;
  *                larger values are clamped to ceil(topk / 32).
  *   head_groups  1: each workgroup computes all 64 heads of its slice (the
- *                pages' one-program-per-query layout, Steps 3-4); 2 or 4:
- *                that many workgroups of 32 or 16 heads share the slice's
- *                gathered records.  0: automatic for the chosen nsplit.
- *                Other values: MLASD_ERR_SHAPE.
+ *                pages' one-program-per-query layout, Steps 3-4); 2: two
+ *                workgroups of 32 heads share the slice's gathered records.
+ *                0: automatic for the chosen nsplit.  Other values:
+ *                MLASD_ERR_SHAPE.
  * Results equal mla_sparse_decode's up to floating-point rounding (the head
  * groups do not change any value; the slices change the summation order).
  * Split plans need scratch as mla_sparse_decode does; mla_sparse_workspace_size
@@ -162,8 +167,8 @@ int mla_sparse_decode_ex(const mlasd_tensor* q, const mlasd_tensor* kv_pages,
  * results as mla_sparse_decode (bit for bit).  It needs no mlasd_prepare:
  * split partials go to a static device array of 16 MiB per GPU, held by
  * the library until the process ends; a call whose plan needs more
- * (B * nsplit * 64 * 449 * 4 bytes > 16 MiB; no automatic plan up to
- * B = 56 at top-k 512 on 256 CUs does) returns MLASD_ERR_WORKSPACE and
+ * (B * nsplit * 64 * 449 * 4 bytes > 16 MiB; no automatic plan on 256 CUs
+ * does: at most 128 slices, 14.7 MB) returns MLASD_ERR_WORKSPACE and
  * enqueues nothing.  It calls no hipMalloc, hipFree or other allocating
  * routine.  Every call on one GPU shares that GPU's array: calls that may
  * overlap in time on one GPU (different streams without ordering, or
@@ -181,7 +186,7 @@ int mla_sparse_decode_noalloc(const mlasd_tensor* q, const mlasd_tensor* kv_page
  * mla_sparse_plan -- the plan the library would use (host only, no device
  * work): writes the number of top-k slices per query, the number of index
  * entries per slice (a multiple of 32) and, if head_groups is not NULL, the
- * number of head groups (1, 2 or 4).  nsplit_request as in
+ * number of head groups (1 or 2).  nsplit_request as in
  * mla_sparse_decode_ex.  num_cus > 0 plans for that many compute units;
  * num_cus <= 0 queries the current HIP device.
  */

@@ -196,7 +196,7 @@ def mla_sparse_decode(q, kv_pages, page_table, topk_idx, seq_lens, softmax_scale
     q bf16 [B,64,512]; kv_pages uint8 [num_pages,149504] (any page stride);
     page_table int32 [B,max_pages]; topk_idx int32 [B,topk]; seq_lens int32
     [B].  `nsplit` forces the number of top-k slices per query and
-    `head_groups` (1, 2, 4) the number of workgroups sharing a slice's heads
+    `head_groups` (1, 2) the number of workgroups sharing a slice's heads
     (None = library plan).  Split plans need scratch reserved with
     prepare() / reserve() on the stream first.
     """

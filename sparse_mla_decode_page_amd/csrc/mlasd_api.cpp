@@ -212,33 +212,14 @@ int reserve_workspace(hipStream_t stream, size_t bytes) {
 // plan
 // ---------------------------------------------------------------------------
 
-// Plan: one workgroup per (query, top-k slice, head group).  Without a
-// request the workgroups of a query are floor(cus / batch), so one round of
-// workgroups covers the GPU:
-//   - two head groups of 32 heads whenever batch * nsplit * 2 fits the CUs:
-//     a 32-head workgroup reads each LDS tile with two head-group waves
-//     instead of four and loads half of Q, and its sibling shares the
-//     gathered records through L2 (measured: c1 12.8 -> 11.2 us, c2 15.6 ->
-//     13.9 us, c3 with 2 slices of 32-head groups 23.8 us against 24.9 us
-//     with 4 slices of 64 heads);
-//   - four head groups of 16 heads instead when a query gets at least 16
-//     workgroups (batch <= cus / 16), and for forced slice counts when
-//     batch * nsplit * 4 still leaves three quarters of the CUs idle: fewer
-//     slices then means fewer fp32 partials to write and merge (measured at
-//     topk 512: B=16 with (4 slices, 4 groups) 12.8 us against 13.2 us with
-//     (8, 2); B=4 10.6 against 11.1 us; but B=32 prefers (4, 2) 15.5 us over
-//     (2, 4) 17.0 us and B=48 (2, 2) 18.8 us over (1, 4) 20.0 us, where a
-//     16-head workgroup has too many tiles to walk alone);
-//   - four head groups and no split when they alone fill the GPU (4 * batch
-//     above 7/8 of the CUs, B = 57..64 on 256): the longer tile walk then costs
-//     less than the split's fp32 partials and combine launch (B=64, 65,536-
-//     token sequences: 20.4 us against 20.7-20.9 us for (2, 2), and 62.8 ->
-//     ~33 MB of HBM traffic per step; B=56: (2, 2) 19.5 us against 20.0 us);
-//   - the rest of the budget in top-k slices, none cut below kMinAutoSlice
-//     entries: every extra slice costs a partial write and read, and below
-//     two tiles a workgroup's fixed start-up cost (index resolution, first
-//     gather) dominates.
-// A slice holds a whole number of 32-token tiles.
+// Plan: one workgroup per (query, top-k slice, head group of 32 or 64
+// heads).  Without a request a query gets floor(cus / batch) workgroups, so
+// one round of workgroups covers the GPU: two head groups of 32 heads when
+// it gets at least two (a 32-head workgroup runs one Q K^T wave and its
+// sibling reads the gathered records from L2), the rest in top-k slices of at
+// least kMinAutoSlice entries (each extra slice costs an fp32 partial write
+// and read, and below two tiles a workgroup's fixed start-up cost
+// dominates).  A slice holds a whole number of 32-token tiles.
 constexpr int kMinAutoSlice = 64;
 
 void make_plan(int32_t batch, int32_t topk, int32_t ns_request, int32_t hg_request, int cus,
@@ -246,13 +227,12 @@ void make_plan(int32_t batch, int32_t topk, int32_t ns_request, int32_t hg_reque
   const int tile = mlasd::kTileTokens;
   const int max_split = topk > 0 ? (topk + tile - 1) / tile : 1;
   const int per_query = batch > 0 ? cus / batch : cus;   // workgroups per query in one round
-  const bool fill_by_groups = ns_request <= 0 && per_query == 4 && (int64_t)batch * 4 * 8 > (int64_t)cus * 7;
-  const bool four_groups = ns_request <= 0 && (per_query >= 16 || fill_by_groups);
+  const int hg = hg_request > 0 ? hg_request : (per_query >= 2 ? 2 : 1);
   int ns;
   if (ns_request > 0) {
     ns = ns_request;
   } else {
-    ns = four_groups ? per_query / 4 : per_query >= 2 ? per_query / 2 : 1;   // fill_by_groups: 1
+    ns = per_query / hg;
     const int by_len = topk > 0 ? (topk + kMinAutoSlice - 1) / kMinAutoSlice : 1;
     if (ns > by_len) ns = by_len;
   }
@@ -263,12 +243,7 @@ void make_plan(int32_t batch, int32_t topk, int32_t ns_request, int32_t hg_reque
   ns = topk > 0 ? (topk + len - 1) / len : 1;
   *nsplit = ns;
   *split_len = len;
-  if (hg_request > 0)
-    *head_groups = hg_request;
-  else if (four_groups || (int64_t)batch * ns * 4 <= cus / 4)
-    *head_groups = 4;
-  else
-    *head_groups = (int64_t)batch * ns * 2 <= cus ? 2 : 1;
+  *head_groups = hg;
 }
 
 // Bytes of split scratch for one call: fp32 partial rows, then fp32 lse values.
@@ -279,7 +254,7 @@ size_t split_scratch_bytes(int32_t batch, int32_t nsplit) {
   return (n_o + n_l) * sizeof(float);
 }
 
-bool valid_head_groups(int32_t hg) { return hg >= 0 && hg <= 4 && hg != 3; }
+bool valid_head_groups(int32_t hg) { return hg >= 0 && hg <= 2; }
 
 // ---------------------------------------------------------------------------
 // decode

@@ -48,7 +48,7 @@ struct DecodeParams {
   float* part_lse;            // [B, nsplit, 64]      when nsplit > 1
   int32_t nsplit;
   int32_t split_len;          // index entries per slice, multiple of kTileTokens
-  int32_t head_groups;        // 1, 2 or 4: workgroups sharing a slice's 64 heads
+  int32_t head_groups;        // 1 or 2: workgroups sharing a slice's 64 heads
 };
 
 struct GatherParams {

@@ -150,7 +150,7 @@ def test_scalar_and_plan_validation_without_device():
     lib = m.load_library()
     assert _decode(lib, _decode_args(), scale=float("nan")) == -4
     assert _decode(lib, _decode_args(), scale=float("inf")) == -4
-    for hg in (3, 5, -1):
+    for hg in (3, 4, 5, -1):
         assert _decode(lib, _decode_args(), nsplit=2, hg=hg) == -2
 
 
@@ -260,26 +260,26 @@ def test_append_zero_tokens_is_a_noop():
 
 
 @pytest.mark.parametrize("batch,topk,req,cus,expect", [
-    (64, 512, 0, 256, (1, 512, 4)),    # 4 workgroups per query filling the GPU: 4 head groups, no split
-    (56, 512, 0, 256, (2, 256, 2)),    # 4 workgroups per query, 224 of 256 CUs: 2 slices x 2 head groups
+    (64, 512, 0, 256, (2, 256, 2)),    # 4 workgroups per query: 2 head groups x 2 slices
+    (56, 512, 0, 256, (2, 256, 2)),
     (64, 512, 0, 240, (1, 512, 2)),    # 3 workgroups per query: 2 head groups, no split
-    (1, 512, 0, 256, (8, 64, 4)),      # small batch: slices of at least 64 entries
-    (16, 512, 0, 256, (4, 128, 4)),    # >= 16 workgroups per query: 16-head workgroups
-    (2, 512, 0, 256, (8, 64, 4)),      # B * nsplit * 4 <= CUs / 4: 16-head workgroups
-    (4, 512, 0, 256, (8, 64, 4)),
-    (17, 512, 0, 256, (6, 96, 2)),     # 15 workgroups per query: slices of 32-head groups
+    (1, 512, 0, 256, (8, 64, 2)),      # small batch: slices of at least 64 entries
+    (16, 512, 0, 256, (8, 64, 2)),
+    (2, 512, 0, 256, (8, 64, 2)),
+    (4, 512, 0, 256, (8, 64, 2)),
+    (17, 512, 0, 256, (6, 96, 2)),     # 15 workgroups per query: 7 slices -> 96-entry slices -> 6
     (32, 512, 0, 256, (4, 128, 2)),
     (128, 512, 0, 256, (1, 512, 2)),   # 2 workgroups per query: head groups, no split
     (100, 512, 0, 256, (1, 512, 2)),
     (129, 512, 0, 256, (1, 512, 1)),   # batch fills the GPU: 64 heads, no split
     (256, 512, 0, 256, (1, 512, 1)),
-    (1, 64, 0, 256, (1, 64, 4)),
-    (3, 300, 0, 256, (5, 64, 4)),      # ragged top-k
-    (3, 45, 0, 256, (1, 64, 4)),
-    (1, 0, 0, 256, (1, 32, 4)),        # empty top-k: one slice, writes zeros / -inf
+    (1, 64, 0, 256, (1, 64, 2)),
+    (3, 300, 0, 256, (5, 64, 2)),      # ragged top-k
+    (3, 45, 0, 256, (1, 64, 2)),
+    (1, 0, 0, 256, (1, 32, 2)),        # empty top-k: one slice, writes zeros / -inf
     (64, 512, 1, 256, (1, 512, 2)),    # forced
-    (64, 512, 3, 256, (3, 192, 1)),    # slices hold whole 32-token tiles
-    (64, 512, 99, 256, (16, 32, 1)),   # clamped to ceil(topk/32)
+    (64, 512, 3, 256, (3, 192, 2)),    # slices hold whole 32-token tiles
+    (64, 512, 99, 256, (16, 32, 2)),   # clamped to ceil(topk/32)
     (8, 100, 0, 80, (2, 64, 2)),       # 10 workgroups per query
     (32, 512, 0, 80, (1, 512, 2)),
 ])

@@ -73,12 +73,12 @@ def _all_codes_pool():
 
 
 def test_gather_dequant_all_codes_all_scales():
-    """The nope part of both operands (K of the nope dims, and V) is the exact
-    dequantised value rounded to nearest-even fp16 (overflow -> inf); K's rope
-    part is the stored bf16 value.  The hook writes K widened to bf16, which
-    is exact: a rounded e4m3 value keeps at most 4 significant bits.  Both
-    are identical to the oracle wherever the value is representable in fp16,
-    which holds for every value the workloads produce."""
+    """Every (e4m3 code, UE8M0 byte) pair: the rows the contractions consume,
+    times the row's power of two, equal the oracle's dequantised values
+    exactly for scale bytes 0..246 -- the pages dequantise to bf16, exact for
+    bytes 3..246 -- NaN codes included.  Bytes 247..254 scale e4m3 values
+    past fp32's range: exact where the value is below 2^128, infinite (with
+    its sign) where it is not."""
     pool = _all_codes_pool()
     pt = np.array([[0, 1]], dtype=np.int32)
     idx = np.arange(510, dtype=np.int32)[None][:, ::-1].copy()
@@ -88,17 +88,67 @@ def test_gather_dequant_all_codes_all_scales():
     torch.cuda.synchronize()
     rows, ok = O.gather_dequant(pool, pt, idx, lens)
     assert ok.all() and valid.cpu().numpy().all()
-    with np.errstate(over="ignore"):
-        r32 = torch.from_numpy(rows.astype(np.float32))
-    exp = np.concatenate([r32[..., :448].to(torch.float16).double().numpy(), rows[..., 448:]], axis=-1)
     gg = got.cpu().double().numpy()
-    nan = np.isnan(exp)
+    nan = np.isnan(rows)
     assert np.array_equal(np.isnan(gg), nan)
-    bad = np.argwhere(gg[~nan] != exp[~nan])
-    assert len(bad) == 0, (len(bad), gg[~nan][bad[:5, 0]], exp[~nan][bad[:5, 0]])
-    # and exactly the oracle's values wherever those are representable
-    same = exp == rows
-    assert np.array_equal(gg[same], rows[same])
+    byte = (510 - 1 - np.arange(510)) % 255           # scale byte of entry j (positions reversed)
+    fits = np.abs(np.where(nan, 0.0, rows)) < 2.0 ** 128
+    assert np.all(fits[0, byte <= 246]), "bytes 0..246 must stay inside fp32's range"
+    same = ~nan & fits
+    bad = np.argwhere(gg[same] != rows[same])
+    assert len(bad) == 0, (len(bad), gg[same][bad[:5, 0]], rows[same][bad[:5, 0]])
+    over = ~nan & ~fits
+    assert np.all(np.isinf(gg[over])) and np.array_equal(np.signbit(gg[over]), np.signbit(rows[over]))
+
+
+def _span_scales(spans, base_lo=-120, base_hi=110):
+    """group_scale for the generator: each record gets a random base
+    exponent and its 7 groups spread over the given span (binades)."""
+    def f(rng, n):
+        base = rng.integers(base_lo, base_hi, n)
+        span = rng.choice(spans, n)
+        off = np.floor(rng.random((n, 7)) * (span[:, None] + 1)).astype(np.int64)
+        off[:, 0] = 0
+        off[np.arange(n), rng.integers(1, 7, n)] = span        # one group at the top of the span
+        return np.ldexp(1.0, base[:, None] + off)
+    return f
+
+
+def test_gather_dequant_rebased_tokens_exact():
+    """Tokens whose 7 groups span up to 22 binades anywhere in UE8M0's range
+    (scale bytes about 0..246) are held exactly: each such token is stored
+    at one power of two of its own and the hook multiplies it back."""
+    w = G.build_workload(77, [4000, 9000], 512, group_scale=_span_scales(np.arange(0, 23)))
+    d = to_device(w)
+    got, valid = mlasd.mla_sparse_gather_dequant(d["kv_pages"], d["page_table"], d["topk_idx"], d["seq_lens"])
+    torch.cuda.synchronize()
+    rows, ok = O.gather_dequant(w.kv_pages, w.page_table, w.topk_idx, w.seq_lens)
+    assert np.array_equal(valid.cpu().numpy().astype(bool), ok)
+    gg = got.cpu().double().numpy()
+    fits = np.abs(rows) < 2.0 ** 128
+    bad = np.argwhere((gg != rows) & fits)
+    assert len(bad) == 0, (len(bad), bad[:5])
+
+
+def test_gather_dequant_wider_spans_keep_the_large_groups():
+    """A token whose groups span more than 22 binades keeps every group within
+    22 binades of its largest exactly; smaller groups are rounded to the
+    fp16 grid of that token (their values are below 2^-22 of its largest)."""
+    w = G.build_workload(78, [3000], 256, group_scale=_span_scales(np.arange(23, 40), -60, 40))
+    d = to_device(w)
+    got, _ = mlasd.mla_sparse_gather_dequant(d["kv_pages"], d["page_table"], d["topk_idx"], d["seq_lens"])
+    torch.cuda.synchronize()
+    rows, ok = O.gather_dequant(w.kv_pages, w.page_table, w.topk_idx, w.seq_lens)
+    gg = got.cpu().double().numpy()
+    flat = w.kv_pages.reshape(-1)
+    for j in range(w.topk):
+        p = int(w.topk_idx[0, j])
+        pg, sl = int(w.page_table[0, p // 256]), p % 256
+        sb = flat[pg * 149504 + 147456 + sl * 8:][:7].astype(int) - 127
+        near = np.repeat(sb >= sb.max() - 22, 64)
+        assert np.array_equal(gg[0, j, :448][near], rows[0, j, :448][near]), j
+        assert np.all(np.abs(gg[0, j, :448][~near] - rows[0, j, :448][~near]) <= 2.0 ** (sb.max() - 22 - 9 + 1)), j
+        assert np.array_equal(gg[0, j, 448:], rows[0, j, 448:])
 
 
 # ----------------------------------------------------------------------------
@@ -122,15 +172,15 @@ def test_decode_forced_split(i, nsplit):
     check_attention(out, lse, ref_out, ref_lse, label=f"config {i} nsplit={nsplit}")
 
 
-@pytest.mark.parametrize("i,nsplit", [(0, 1), (1, 1), (1, 8), (2, 4), (2, 8), (3, 2), (3, 1)])
+@pytest.mark.parametrize("i,nsplit", [(0, 1), (1, 1), (1, 8), (2, 4), (2, 8), (3, 2), (3, 1), (4, 1)])
 def test_head_groups_bitwise_equal(i, nsplit):
-    """Two 32-head or four 16-head workgroups per slice compute exactly what
-    one 64-head workgroup computes: the same tiles in the same order with the
-    same instructions per head, so the results agree bit for bit."""
+    """Two 32-head workgroups per slice compute exactly what one 64-head
+    workgroup computes: the same tiles in the same order with the same
+    instructions per head, so the results agree bit for bit."""
     w, (ref_out, ref_lse) = config(i)
     print(f"head groups config {i} nsplit={nsplit}", flush=True)
     d = to_device(w)
-    r = [decode(d, w.softmax_scale, nsplit=nsplit, head_groups=hg) for hg in (1, 2, 4)]
+    r = [decode(d, w.softmax_scale, nsplit=nsplit, head_groups=hg) for hg in (1, 2)]
     torch.cuda.synchronize()
     for o, l in r[1:]:
         assert torch.equal(r[0][0], o) and torch.equal(r[0][1], l)
@@ -138,15 +188,16 @@ def test_head_groups_bitwise_equal(i, nsplit):
 
 
 def _custom(seed, lens, topk, **kw):
+    """A seeded workload whose pool holds the sequences' pages plus two spare."""
     need = sum((L + 255) // 256 for L in lens)
     return G.build_workload(seed, lens, topk, num_pages=need + 2, **kw)
 
 
-def _check_custom(w, nsplit=None, label=""):
+def _check_custom(w, nsplit=None, label="", maxnorm=False):
     ref_out, ref_lse = O.sparse_mla_decode(w.q_bits, w.kv_pages, w.page_table, w.topk_idx,
                                            w.seq_lens, w.softmax_scale)
     out, lse = run(w, nsplit=nsplit)
-    return check_attention(out, lse, ref_out, ref_lse, label=label)
+    return check_attention(out, lse, ref_out, ref_lse, label=label, maxnorm=maxnorm)
 
 
 @pytest.mark.parametrize("topk", [1, 2, 31, 33, 45, 100, 257, 511])
@@ -228,13 +279,13 @@ def test_softmax_scale_values(scale):
     _check_custom(w, label=f"scale={scale}")
 
 
-@pytest.mark.parametrize("q_log2", [8, -6, "tiny"])
+@pytest.mark.parametrize("q_log2", [8, -6, 20, -40, 100, -100, "tiny"])
 def test_query_magnitudes(q_log2):
-    """Q's nope dims enter QK^T in fp16: exact for bf16 magnitudes in
-    [2^-14, 65504], every bit kept down to 2^-24 below that.  Q scaled by 2^8
-    (values up to ~1,200) or 2^-6, with the softmax scale compensating, and Q
-    with 5 % of its entries replaced by values near 1e-6 all meet the oracle
-    bar."""
+    """q enters Q K^T scaled per head by a power of two (its largest nope
+    value lands in [2^15, 2^16)), exact over bf16's range: q scaled by 2^8,
+    2^-6, 2^20 (|q| near 4e6), 2^-40 and 2^+-100, with the softmax scale
+    compensating, and q with 5 % of its entries replaced by values near 1e-6
+    all meet the oracle bar."""
     w = _custom(21, [5000, 30000], 256)
     q = (w.q_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     if q_log2 == "tiny":
@@ -246,6 +297,54 @@ def test_query_magnitudes(q_log2):
         w.softmax_scale = w.softmax_scale * 2.0 ** -q_log2
     w.q_bits = G.bf16_bits(q)
     _check_custom(w, label=f"q scaled {q_log2}")
+
+
+def _wide_range_workload(seed, lens, topk, q_log2):
+    """Group amax log-uniform over 1e-4 .. 1e5 (scale bytes ~105 .. 135,
+    independently per token and group), q times 2^q_log2, and a softmax
+    scale that brings the largest score to about 30."""
+    w = _custom(seed, lens, topk, group_scale=lambda r, n: 10.0 ** r.uniform(-4.0, 5.0, (n, 7)))
+    q = (w.q_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64) * 2.0 ** q_log2
+    w.q_bits = G.bf16_bits(q)
+    rows, ok = O.gather_dequant(w.kv_pages, w.page_table, w.topk_idx, w.seq_lens)
+    qd = O.bf16_value(w.q_bits)
+    smax = max(np.abs(qd[b] @ rows[b][ok[b]].T).max() for b in range(w.batch) if ok[b].any())
+    w.softmax_scale = 30.0 / smax
+    return w
+
+
+@pytest.mark.parametrize("q_log2", [0, 20])
+def test_wide_dynamic_range_cache(q_log2):
+    """A cache whose 64-dim groups have amax from 1e-4 to 1e5 (outside fp16's
+    exact window on both sides) and q up to ~4e6, with the softmax scale
+    compensating: lse meets the elementwise bar, out the per-query max-norm
+    bar (values near 1e5 cancel)."""
+    w = _wide_range_workload(4400 + q_log2, [3000, 20000, 700], 512, q_log2)
+    print(f"wide range: softmax_scale={w.softmax_scale:.3e}", flush=True)
+    for ns in (None, 1, 4):
+        _check_custom(w, nsplit=ns, label=f"wide range q*2^{q_log2} nsplit={ns}", maxnorm=True)
+
+
+def test_rebased_and_plain_tiles_mixed():
+    """Slices whose tiles alternate between plain tokens and tokens that need
+    a power-of-two rebase (tiny groups near 1e-9, large ones near 1e6), in
+    both orders, so the running reference rises, stays and multiplies O
+    back: the oracle bar (max-norm form: values up to 1e6) holds and 32/64-head
+    workgroups agree bit for bit."""
+    def gs(rng, n):
+        kind = rng.integers(0, 3, n)
+        scale = np.where(kind == 0, 1.0, np.where(kind == 1, 1e-9, 1e6))
+        return np.repeat(scale[:, None], 7, axis=1) * 10.0 ** rng.uniform(-0.5, 0.5, (n, 7))
+    w = _custom(4500, [2000, 9000, 300], 512, group_scale=gs)
+    rows, ok = O.gather_dequant(w.kv_pages, w.page_table, w.topk_idx, w.seq_lens)
+    qd = O.bf16_value(w.q_bits)
+    w.softmax_scale = 30.0 / max(np.abs(qd[b] @ rows[b][ok[b]].T).max() for b in range(w.batch))
+    d = to_device(w)
+    r = [decode(d, w.softmax_scale, nsplit=1, head_groups=hg) for hg in (1, 2)]
+    torch.cuda.synchronize()
+    assert torch.equal(r[0][0], r[1][0]) and torch.equal(r[0][1], r[1][1])
+    for ns in (None, 1, 2):
+        _check_custom(w, nsplit=ns, label=f"mixed rebased tiles nsplit={ns}", maxnorm=True)
 
 
 def test_outliers_small_batch():
@@ -518,7 +617,7 @@ def test_validation_matrix(batch, topk):
     ref_out, ref_lse = O.sparse_mla_decode(w.q_bits, w.kv_pages, w.page_table, w.topk_idx,
                                            w.seq_lens, w.softmax_scale)
     d = to_device(w)
-    for ns, hg in ((None, None), (1, 1), (1, 2), (1, 4)):
+    for ns, hg in ((None, None), (1, 1), (1, 2)):
         out, lse = decode(d, w.softmax_scale, nsplit=ns, head_groups=hg)
         torch.cuda.synchronize()
         check_attention(out, lse, ref_out, ref_lse,
