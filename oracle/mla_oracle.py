@@ -55,6 +55,14 @@ R7-R12 cover the output format, tolerances, record order and the kernel):
       values are stored as they are.  A token is written at position p of
       sequence s when 0 <= s < B, p >= 0, p // 256 < max_pages and the
       physical page lies in the pool; otherwise it is skipped.
+  R14 (top-k selection, upstream of the decode) The indexer scores every
+      position of a query's context in fp32 ("The Turning Point", "The
+      Strategic Context: Why This Message Exists", item 3) and the top-k
+      positions become topk_idx.  Read here: positions 0 .. L-1 with
+      L = min(max(seq_len, 0), max_len) are candidates; they are ranked by
+      score, higher first, equal scores by position, lower first (a NaN score
+      ranks as -inf, -0.0 equals +0.0); the first min(k, L) positions in rank
+      order are written, in that order, and the rest of the k slots get -1.
 """
 from __future__ import annotations
 
@@ -289,3 +297,24 @@ def kv_append(kv_pages, page_table, seq_ids, positions, latent_bits):
         kv[page, SCALE_REGION + slot * SCALE_RECORD_BYTES:SCALE_REGION + (slot + 1) * SCALE_RECORD_BYTES] = sc
     return kv
 
+
+# ----------------------------------------------------------------------------
+# top-k selection (reading R14)
+# ----------------------------------------------------------------------------
+
+def topk_select(scores, seq_lens, k):
+    """scores fp32 [B, max_len], seq_lens [B], k -> topk_idx int32 [B, k]:
+    each row's candidate positions sorted by (score descending, position
+    ascending), the first min(k, L) kept, -1 after them (reading R14)."""
+    sc = np.asarray(scores, dtype=np.float32)
+    B, max_len = sc.shape
+    out = np.full((B, k), -1, dtype=np.int32)
+    for b in range(B):
+        L = min(max(int(seq_lens[b]), 0), max_len)
+        v = sc[b, :L].astype(np.float64)
+        v = np.where(np.isnan(v), -np.inf, v)
+        pos = np.arange(L)
+        order = np.lexsort((pos, -v))   # primary key -v (higher score first), then position
+        n = min(k, L)
+        out[b, :n] = pos[order[:n]]
+    return out

@@ -494,3 +494,78 @@ def test_append_writes_valid_tokens_only_and_decodes_back():
         mask[page, slot * 576:(slot + 1) * 576] = False
         mask[page, 147456 + slot * 8:147456 + slot * 8 + 8] = False
     assert np.all(out[mask] == 0x5A)
+
+
+# ----------------------------------------------------------------------------
+# top-k selection (reading R14)
+# ----------------------------------------------------------------------------
+
+def _golden_topk():
+    with open(os.path.join(GOLDEN, "topk_example.json")) as f:
+        g = json.load(f)
+    scores = np.array([[float(v) for v in row] for row in g["scores"]], dtype=np.float32)
+    return scores, g["cases"]
+
+
+def test_topk_select_hand_worked_rows():
+    """Rows worked out by hand from the ranking rule: ties by position, NaN
+    as -inf after -inf's position order, -0.0 tied with +0.0, short and
+    empty sequences padded with -1."""
+    scores, cases = _golden_topk()
+    for c in cases:
+        got = O.topk_select(scores, c["seq_lens"], c["k"])
+        assert got.tolist() == c["expected"], c
+
+
+def _check_topk_properties(scores, seq_lens, k, got):
+    """Properties that together fix the selection uniquely: the right count,
+    -1 only as padding, distinct in-range positions, non-increasing scores
+    with increasing positions among equal scores, every selected score >= every
+    unselected one, and at the boundary score the lowest positions win."""
+    B, max_len = scores.shape
+    for b in range(B):
+        L = min(max(int(seq_lens[b]), 0), max_len)
+        n = min(k, L)
+        row = got[b]
+        assert (row[:n] >= 0).all() and (row[n:] == -1).all()
+        sel = row[:n].astype(np.int64)
+        assert len(set(sel.tolist())) == n and (sel < L).all()
+        v = scores[b, :L].astype(np.float64)
+        v = np.where(np.isnan(v), -np.inf, v)
+        s = v[sel]
+        for i in range(n - 1):
+            assert s[i] > s[i + 1] or (s[i] == s[i + 1] and sel[i] < sel[i + 1])
+        rest = np.setdiff1d(np.arange(L), sel)
+        if n and len(rest):
+            assert s.min() >= v[rest].max()
+            tie = rest[v[rest] == s.min()]
+            if len(tie):
+                assert sel[s == s.min()].max() < tie.min()
+
+
+def test_topk_select_properties_with_many_ties():
+    """Random rows drawn from a handful of values (so most scores tie), with
+    NaN, infinities and signed zeros sprinkled in, over every kind of
+    sequence length (negative, 0, below k, above max_len)."""
+    rng = np.random.default_rng(71)
+    vals = np.array([-np.inf, -2.0, -0.0, 0.0, 0.5, 1.0, 1.0 + 2 ** -20, np.inf, np.nan], dtype=np.float32)
+    for trial in range(40):
+        B, max_len, k = int(rng.integers(1, 5)), int(rng.integers(1, 300)), int(rng.integers(1, 70))
+        scores = vals[rng.integers(0, len(vals), (B, max_len))]
+        seq_lens = rng.integers(-3, max_len + 10, B)
+        got = O.topk_select(scores, seq_lens, k)
+        assert got.shape == (B, k) and got.dtype == np.int32
+        _check_topk_properties(scores, seq_lens, k, got)
+
+
+def test_topk_select_distinct_scores_match_a_full_sort():
+    """With distinct scores the selection is the k largest in descending
+    order: compared with numpy's argsort of the negated row."""
+    rng = np.random.default_rng(72)
+    scores = rng.permutation(4096).astype(np.float32).reshape(4, 1024) * 0.25 - 300.0
+    seq_lens = np.array([1024, 700, 5, 1024])
+    got = O.topk_select(scores, seq_lens, 512)
+    for b in range(4):
+        L = int(seq_lens[b])
+        ref = np.argsort(-scores[b, :L], kind="stable")[:512]
+        assert got[b, :len(ref)].tolist() == ref.tolist()
