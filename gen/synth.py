@@ -348,3 +348,18 @@ def rotation_sets(w: Workload, n_sets, seed):
                             topk_idx=idx, seq_lens=w.seq_lens, softmax_scale=w.softmax_scale,
                             meta=dict(w.meta, rotation=True)))
     return out
+
+
+def indexer_scores(seed, batch, max_len, kind="normal"):
+    """Seeded fp32 per-position scores [batch, max_len] standing in for an
+    indexer's output: "normal" (standard normal, ties rare), "ties" (a
+    handful of values, ties everywhere) or "special" ("ties" plus NaN,
+    infinities and signed zeros)."""
+    rng = _rng(seed)
+    if kind == "normal":
+        return rng.standard_normal((batch, max_len)).astype(np.float32)
+    vals = [-1.5, -0.25, 0.5, 0.5 + 2 ** -20, 3.0]
+    if kind == "special":
+        vals += [np.nan, np.inf, -np.inf, -0.0, 0.0]
+    vals = np.array(vals, dtype=np.float32)
+    return vals[rng.integers(0, len(vals), (batch, max_len))]

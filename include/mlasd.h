@@ -250,6 +250,26 @@ int mla_kv_append(const mlasd_tensor* latent, const mlasd_tensor* seq_ids,
                   const mlasd_tensor* kv_pages, mlasd_stream_t stream);
 
 /*
+ * mla_topk_select -- the other step before the decode: each query's top-k
+ * index list from its indexer scores (the indexer scores every position of
+ * the context in fp32: "The Turning Point", "The Strategic Context: Why
+ * This Message Exists", item 3).
+ *
+ *   scores    F32 [B, max_len], innermost contiguous: one score per position.
+ *   seq_lens  I32 [B]: positions 0 .. L-1, L = min(max(seq_len, 0), max_len),
+ *             are the candidates.  Any stride.
+ *   topk_idx  I32 [B, k], 0 <= k <= 512, innermost contiguous (written): the
+ *             first min(k, L) candidates in rank order -- higher score
+ *             first, equal scores lower position first, a NaN score ranking
+ *             as -inf, -0.0 equal to +0.0 -- then -1.
+ *   stream    HIP stream to enqueue on.
+ * B == 0 or k == 0 is a no-op.  Allocates nothing and never synchronises.
+ * Returns MLASD_OK or a negative MLASD_ERR_* code.
+ */
+int mla_topk_select(const mlasd_tensor* scores, const mlasd_tensor* seq_lens, const mlasd_tensor* topk_idx,
+                    mlasd_stream_t stream);
+
+/*
  * mlasd_prepare -- reserve the split scratch of `stream` (on the current
  * device) for every automatically planned mla_sparse_decode call with
  * batch <= max_batch and topk <= max_topk.  Everything a captured call needs

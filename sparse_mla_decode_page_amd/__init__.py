@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     mla_sparse_decode,
     mla_sparse_decode_noalloc,
     mla_sparse_gather_dequant,
+    mla_topk_select,
     plan,
     prepare,
     release,
@@ -22,6 +23,7 @@ from ._binding import (  # noqa: F401
     workspace_size,
 )
 
-__all__ = ["mla_sparse_decode", "mla_sparse_decode_noalloc", "mla_sparse_gather_dequant", "mla_kv_append", "plan", "prepare",
+__all__ = ["mla_sparse_decode", "mla_sparse_decode_noalloc", "mla_sparse_gather_dequant", "mla_kv_append",
+           "mla_topk_select", "plan", "prepare",
            "reserve", "release", "workspace_bytes", "workspace_size", "describe", "Tensor",
            "load_library", "library_path", "status_string", "MlasdError"]

@@ -64,12 +64,13 @@ def load_library():
     lib.mla_sparse_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
     lib.mla_sparse_gather_dequant.argtypes = [T, T, T, T, T, T, vp]
     lib.mla_kv_append.argtypes = [T, T, T, T, T, vp]
+    lib.mla_topk_select.argtypes = [T, T, T, vp]
     lib.mlasd_prepare.argtypes = [vp, i32, i32]
     lib.mlasd_reserve.argtypes = [vp, sz]
     lib.mlasd_release.argtypes = [vp]
     lib.mlasd_workspace_bytes.argtypes = [vp, ctypes.POINTER(sz)]
     for name in ("mla_sparse_decode", "mla_sparse_decode_ex", "mla_sparse_decode_noalloc", "mla_sparse_plan",
-                 "mla_sparse_workspace_size", "mla_sparse_gather_dequant", "mla_kv_append",
+                 "mla_sparse_workspace_size", "mla_sparse_gather_dequant", "mla_kv_append", "mla_topk_select",
                  "mlasd_prepare", "mlasd_reserve", "mlasd_release", "mlasd_workspace_bytes"):
         getattr(lib, name).restype = ctypes.c_int
     lib.mlasd_status_string.argtypes = [ctypes.c_int]
@@ -262,3 +263,20 @@ def mla_kv_append(latent, seq_ids, positions, page_table, kv_pages, stream=None)
         rc = lib.mla_kv_append(*[ctypes.byref(d) for d in descs], _stream(stream, dev))
     _check(rc, "mla_kv_append")
     return kv_pages
+
+
+def mla_topk_select(scores, seq_lens, k=MAX_TOPK, out=None, stream=None):
+    """Each query's top-k positions from its indexer scores (fp32 [B,
+    max_len]; candidates 0 .. min(seq_len, max_len) - 1): int32 [B, k] in
+    rank order (higher score first, ties by lower position), -1 padded."""
+    dev = _same_device(scores, seq_lens)
+    B = scores.shape[0] if scores.dim() == 2 else -1
+    if out is None:
+        out = torch.empty((B, int(k)), dtype=torch.int32, device=dev)
+    _same_device(out, scores)
+    lib = load_library()
+    descs = [describe(t) for t in (scores, seq_lens, out)]
+    with torch.cuda.device(dev):
+        rc = lib.mla_topk_select(*[ctypes.byref(d) for d in descs], _stream(stream, dev))
+    _check(rc, "mla_topk_select")
+    return out

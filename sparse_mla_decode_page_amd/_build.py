@@ -6,7 +6,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB_NAME = "libmlasd.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["mlasd_decode.hip", "mlasd_combine.hip", "mlasd_append.hip", "mlasd_noalloc.hip", "mlasd_api.cpp"]
+SOURCES = ["mlasd_decode.hip", "mlasd_combine.hip", "mlasd_append.hip", "mlasd_topk.hip", "mlasd_noalloc.hip", "mlasd_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 VALU forms are disabled for every HIP translation unit.  The

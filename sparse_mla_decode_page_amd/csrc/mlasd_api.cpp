@@ -512,6 +512,42 @@ int mla_kv_append(const mlasd_tensor* latent, const mlasd_tensor* seq_ids, const
   return MLASD_OK;
 }
 
+int mla_topk_select(const mlasd_tensor* scores, const mlasd_tensor* seq_lens, const mlasd_tensor* topk_idx,
+                    mlasd_stream_t stream) {
+  if (scores == nullptr || topk_idx == nullptr) return MLASD_ERR_NULL;
+  if (scores->ndim != 2 || scores->shape[0] < 0 || scores->shape[0] > INT32_MAX || scores->shape[1] > INT32_MAX)
+    return MLASD_ERR_SHAPE;
+  const int64_t B = scores->shape[0];
+  const int64_t wsc[2] = {B, -1};
+  int rc = check_tensor(scores, MLASD_F32, 2, wsc, true);
+  if (rc != MLASD_OK) return rc;
+  const int64_t wl[1] = {B};
+  rc = check_tensor(seq_lens, MLASD_I32, 1, wl, true, false);
+  if (rc != MLASD_OK) return rc;
+  if (topk_idx->ndim != 2 || topk_idx->shape[1] < 0 || topk_idx->shape[1] > MLASD_MAX_TOPK) return MLASD_ERR_SHAPE;
+  const int64_t wi[2] = {B, -1};
+  rc = check_tensor(topk_idx, MLASD_I32, 2, wi, true);
+  if (rc != MLASD_OK) return rc;
+  if (B == 0 || topk_idx->shape[1] == 0) return MLASD_OK;
+  if (!aligned(scores->data, 4) || !aligned(seq_lens->data, 4) || !aligned(topk_idx->data, 4)) return MLASD_ERR_ALIGN;
+  int cus = 0;
+  rc = device_cus(&cus);
+  if (rc != MLASD_OK) return rc;
+  mlasd::TopkParams p{};
+  p.scores = (const float*)scores->data;
+  p.sc_sb = scores->stride[0];
+  p.max_len = (int32_t)scores->shape[1];
+  p.seq_lens = (const int32_t*)seq_lens->data;
+  p.len_s = seq_lens->stride[0];
+  p.batch = (int32_t)B;
+  p.topk_idx = (int32_t*)topk_idx->data;
+  p.idx_sb = topk_idx->stride[0];
+  p.k = (int32_t)topk_idx->shape[1];
+  hipError_t e = mlasd::launch_topk(p, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return MLASD_OK;
+}
+
 int mlasd_prepare(mlasd_stream_t stream, int32_t max_batch, int32_t max_topk) {
   if (max_batch < 0 || max_topk < 0 || max_topk > MLASD_MAX_TOPK) return MLASD_ERR_SHAPE;
   int cus = 0;

@@ -89,6 +89,18 @@ struct AppendParams {
   int64_t page_stride;
 };
 
+struct TopkParams {
+  const float* scores;        // fp32 [B, max_len], innermost contiguous
+  int64_t sc_sb;
+  int32_t max_len;
+  const int32_t* seq_lens;    // [B]
+  int64_t len_s;
+  int32_t batch;
+  int32_t* topk_idx;          // [B, k], innermost contiguous
+  int64_t idx_sb;
+  int32_t k;                  // 1 .. 512
+};
+
 // Split scratch of the entry point that allocates nothing: a static device
 // array per GPU (mlasd_noalloc.hip).  noalloc_scratch returns its device
 // address on device `dev`, which must be current.
@@ -100,5 +112,6 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_combine(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_gather(const GatherParams& p, hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
+hipError_t launch_topk(const TopkParams& p, hipStream_t stream);
 
 }  // namespace mlasd

@@ -289,3 +289,26 @@ def test_plan(batch, topk, req, cus, expect):
     assert sl % 32 == 0 and ns * sl >= topk and (ns - 1) * sl < max(topk, 1)
     if req == 0:
         assert batch * ns * hg <= max(cus, batch)   # one round of workgroups
+
+
+def _topk(lib, scores, lens, idx):
+    r = ctypes.byref
+    return lib.mla_topk_select(r(scores) if scores is not None else None, r(lens), r(idx), None)
+
+
+def test_topk_select_validation_without_device():
+    """mla_topk_select's argument checks, all before any device work."""
+    lib = m.load_library()
+    ok = dict(scores=_t(0x10000, F32, [4, 1000]), lens=_t(0x20000, I32, [4]), idx=_t(0x30000, I32, [4, 512]))
+    assert _topk(lib, None, ok["lens"], ok["idx"]) == -1
+    assert _topk(lib, _t(0x10000, I32, [4, 1000]), ok["lens"], ok["idx"]) == -2      # scores dtype
+    assert _topk(lib, _t(0x10000, F32, [4000]), ok["lens"], ok["idx"]) == -2         # scores rank
+    assert _topk(lib, _t(0x10000, F32, [4, 1000], [1000, 2]), ok["lens"], ok["idx"]) == -2   # not contiguous
+    assert _topk(lib, ok["scores"], _t(0x20000, I32, [3]), ok["idx"]) == -2          # seq_lens length
+    assert _topk(lib, ok["scores"], ok["lens"], _t(0x30000, I32, [4, 513])) == -2    # k > 512
+    assert _topk(lib, ok["scores"], ok["lens"], _t(0x30000, I32, [5, 512])) == -2    # batch mismatch
+    assert _topk(lib, ok["scores"], ok["lens"], _t(0x30000, F32, [4, 512])) == -2    # out dtype
+    assert _topk(lib, ok["scores"], ok["lens"], _t(0x30002, I32, [4, 512])) == -3    # out misaligned
+    # empty work is a no-op
+    assert _topk(lib, _t(0, F32, [0, 1000]), _t(0, I32, [0]), _t(0, I32, [0, 512])) == 0
+    assert _topk(lib, ok["scores"], ok["lens"], _t(0x30000, I32, [4, 0])) == 0

@@ -1,0 +1,97 @@
+"""Top-k selection (the step before the decode) against the oracle, bit for
+bit: random and tie-heavy score rows, NaN / infinities / signed zeros, short,
+empty and clamped sequences, the full B=64 x 65,536 shape, and the selection
+chained before the decode in one captured graph."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import sparse_mla_decode_page_amd as mlasd
+from gen import synth as G
+from helpers import check_attention, reserve_for, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _select(scores, lens, k):
+    s = torch.from_numpy(np.ascontiguousarray(scores)).cuda()
+    l = torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda()
+    out = mlasd.mla_topk_select(s, l, k)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _check(scores, lens, k, label):
+    print(f"topk: {label} B={scores.shape[0]} max_len={scores.shape[1]} k={k}", flush=True)
+    got = _select(scores, lens, k)
+    ref = O.topk_select(scores, lens, k)
+    bad = np.argwhere(got != ref)
+    assert len(bad) == 0, f"{label}: {len(bad)} slots differ, first at {bad[:3].tolist()}"
+
+
+@pytest.mark.parametrize("k", [1, 7, 100, 512])
+def test_random_rows(k):
+    sc = G.indexer_scores(11, 6, 5000)
+    _check(sc, [5000, 4999, 600, 100, 0, -3], k, "random")
+
+
+@pytest.mark.parametrize("kind", ["ties", "special"])
+@pytest.mark.parametrize("k", [33, 512])
+def test_tie_heavy_rows(kind, k):
+    sc = G.indexer_scores(12, 5, 3000, kind)
+    _check(sc, [3000, 2048, 513, 512, 40], k, kind)
+
+
+def test_short_empty_and_clamped_lengths():
+    sc = G.indexer_scores(13, 6, 700, "special")
+    _check(sc, [10 ** 6, 700, 701, 1, 0, -1], 512, "lengths")
+    _check(G.indexer_scores(14, 3, 1), [1, 5, 0], 4, "max_len 1")
+
+
+def test_full_shape_b64_65536():
+    sc = G.indexer_scores(15, 64, 65536)
+    lens = np.full(64, 65536)
+    lens[::7] = np.random.default_rng(15).integers(0, 65536, len(lens[::7]))
+    _check(sc, lens, 512, "B=64 x 65536")
+
+
+def test_full_length_ties():
+    """Rows of 65,536 scores from five values: the k-th score is shared by
+    thousands of positions, of which the lowest fill the list."""
+    sc = G.indexer_scores(16, 8, 65536, "ties")
+    _check(sc, [65536, 65535, 40000, 513, 65536, 30000, 9000, 70000], 512, "ties 65536")
+
+
+def test_chained_before_the_decode_in_one_graph():
+    """scores -> topk_idx -> decode captured in one HIP graph, replayed with
+    eager work in between: every replay's out / lse meet the oracle bar for
+    the oracle's selection of the same scores."""
+    lens = [3000, 700, 9000, 0]
+    need = sum((L + 255) // 256 for L in lens)
+    w = G.build_workload(17, lens, 512, num_pages=need + 2, fill="all")
+    d = to_device(w)
+    scores = G.indexer_scores(18, len(lens), 9500)
+    ref_idx = O.topk_select(scores, w.seq_lens, 512)
+    ref_out, ref_lse = O.sparse_mla_decode(w.q_bits, w.kv_pages, w.page_table, ref_idx, w.seq_lens,
+                                           w.softmax_scale)
+    sc = torch.from_numpy(scores).cuda()
+    idx = torch.empty((len(lens), 512), dtype=torch.int32, device="cuda")
+    out = torch.empty((len(lens), 64, 448), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((len(lens), 64), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.Stream()
+    reserve_for(len(lens), 512, stream=stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        mlasd.mla_topk_select(sc, d["seq_lens"], 512, out=idx, stream=stream)
+        mlasd.mla_sparse_decode(d["q"], d["kv_pages"], d["page_table"], idx, d["seq_lens"], w.softmax_scale,
+                                out=out, lse=lse, stream=stream)
+    for rep in range(3):
+        idx.fill_(-7)
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(idx.cpu().numpy(), ref_idx), f"replay {rep}: topk_idx differs"
+        check_attention(out, lse, ref_out, ref_lse, label=f"chained replay {rep}")
+        torch.ones(1 << 20, device="cuda").sum()   # eager work between replays
