@@ -203,6 +203,43 @@ def bench_append(dev, kv, pt, seq_len, steps, stream):
             "workload": f"{B} sequences x {per_seq} new tokens into the resident pool"}
 
 
+def bench_topk(dev, stream, steps, batch=64, max_len=65536, k=512):
+    """Time mla_topk_select on `batch` rows of `max_len` fp32 scores (all
+    positions candidates): HIP events on the launch stream around `steps`
+    calls captured in one graph."""
+    import torch
+    import sparse_mla_decode_page_amd as mlasd
+    from gen.synth import indexer_scores
+    sc = torch.from_numpy(indexer_scores(31, batch, max_len)).to(dev)
+    lens = torch.full((batch,), max_len, dtype=torch.int32, device=dev)
+    idx = torch.empty((batch, k), dtype=torch.int32, device=dev)
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            mlasd.mla_topk_select(sc, lens, k, out=idx, stream=stream)
+    stream.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(steps):
+            mlasd.mla_topk_select(sc, lens, k, out=idx, stream=stream)
+    with torch.cuda.stream(stream):
+        g.replay()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+    stream.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    byts = batch * max_len * 4 + batch * k * 4 + batch * 4
+    gbs = byts / (us * 1e-6) / 1e9
+    del g
+    return {"workload": f"{batch} queries x {max_len} fp32 scores, k={k}", "us_per_launch": us,
+            "rows_per_s": batch / (us * 1e-6),
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": byts},
+            "launch": f"HIP graph replay of {steps} calls"}
+
+
 class Workbench:
     """One workload on the device: rotating input sets, the step function,
     and the graph of exactly `steps` steps."""
@@ -269,7 +306,8 @@ class Workbench:
                     self.step(i, side)
                 ev1.record(side)
             side.synchronize()
-            return dict(ms_step=ev0.elapsed_time(ev1) / steps, warmup_steps=warmup, order=range(steps))
+            return dict(ms_step=ev0.elapsed_time(ev1) / steps, warmup_steps=warmup,
+                        order=[i % self.n_sets for i in range(steps)])
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=side):
             for i in range(steps):
@@ -394,8 +432,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager calls (counter-collection runs)")
     ap.add_argument("--no-append", action="store_true", help="skip the cache-append measurement")
-    ap.add_argument("--op", choices=["decode", "append"], default="decode",
-                    help="append: time only the cache-append kernel (on workload c3's pool)")
+    ap.add_argument("--op", choices=["decode", "append", "topk"], default="decode",
+                    help="append: time only the cache-append kernel (on workload c3's pool); "
+                         "topk: time only the top-k selection (64 x 65,536 scores)")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the flushed single-call timing and the copy ceiling (profiling runs)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -441,6 +480,11 @@ def main():
         res["metric"] = "cache append: tokens/s"
         print(json.dumps(res), flush=True)
         return
+    if args.op == "topk":
+        res = bench_topk(dev, torch.cuda.Stream(dev), args.steps)
+        res["metric"] = "top-k selection: query rows/s"
+        print(json.dumps(res), flush=True)
+        return
 
     if args.batch > 0:
         lens = np.full(args.batch, args.seq_len)
@@ -472,6 +516,7 @@ def main():
                 s["cold_call"] = cold_calls(wb.step, wb.n_sets, wb.stream, dev)
         if key == "config3" and not args.no_append:
             per["kv_append"] = bench_append(dev, wb.kv, wb.pt, int(w.seq_lens.min()), 50, wb.stream)
+            per["topk_select"] = bench_topk(dev, wb.stream, 50)
         if key != head_key:
             del wb
             torch.cuda.empty_cache()
