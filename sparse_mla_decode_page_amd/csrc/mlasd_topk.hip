@@ -6,27 +6,55 @@
 // lower first (NaN ranks as -inf, -0.0 equals +0.0); the first min(k, L)
 // positions in rank order are written in that order, then -1.
 //
-// One workgroup per query.  Each score maps to a 32-bit key whose unsigned
-// order is the rank order of the scores.  A three-digit radix select (11,
-// 11 and 10 bits, histograms in LDS) finds the k-th largest key T; one more
-// pass in position order collects every key above T and, of the keys equal
-// to T, the lowest positions that complete k (block-wide prefix sums keep
-// position order); a bitonic sort of the <= 512 picks by (key, -position)
-// gives the output order.  Rows of at most k candidates skip the select.
+// One workgroup per query.  Each candidate becomes a 64-bit composite,
+// (key << 32) | (2^32 - 1 - position), key a 32-bit map of the score whose
+// unsigned order is the score order: composites are distinct and their
+// unsigned order is the rank order, so the picks are exactly the min(k, L)
+// largest composites.
+//   1. Threshold guess (rows over kCand positions): the composites of 512
+//      positions spread over the row; t0, the lower edge of the 22-bit bin
+//      holding their r-th largest, r set so about 3 k of the row's
+//      composites lie at or above t0.
+//   2. One pass over the row (its only read from HBM) appends every
+//      composite >= t0 to an LDS candidate list, one LDS atomic per wave
+//      and batch.  Since t0's low 42 bits are 0, the test is a float
+//      comparison with the score whose key t0 holds, unless that score is
+//      zero or denormal.  Shorter rows go to the list whole.
+//   3. If the list holds at least k and at most kCand composites, a radix
+//      select over it (11/11/10-bit digits over the 64 bits, LDS
+//      histograms, stopping once a digit's bin is taken whole) gives the
+//      k-th largest composite Tc, and the picks are the list's composites
+//      >= Tc.  Otherwise (guess too high or too low, e.g. long rows of
+//      equal scores) the same select and collection run over the row.
+//   4. A bitonic sort of the <= 512 picks, descending, gives the output
+//      order: stages within a wave by DPP and lane swizzles, the six with
+//      strides of 64 and more through LDS.
+// A row is read as a head of up to 3 positions before its first 16-byte
+// boundary, a body of float4 vectors and a tail of up to 3 positions.
 #include "mlasd_internal.h"
 
 namespace mlasd {
 namespace {
 
-constexpr int kTopkThreads = 1024;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kTopkThreads = 512;
 constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kBins = 2048;
+constexpr int kCand = 16384;       // LDS candidate list (128 KiB)
+constexpr int kSample = kTopkThreads;
+constexpr int kUnroll = 8;         // float4 loads in flight per thread in a compaction pass
+constexpr int kSweepUnroll = 2;    // and in a histogram pass over the row (the rare path)
 
 struct TopkSmem {
+  uint64_t cand[kCand];
+  uint64_t sel[kMaxTopk];
   uint32_t hist[kBins];
-  uint64_t sel[kMaxTopk];      // (key << 32) | (0xffffffff - position): larger = earlier in rank order
-  uint32_t wave_sum[kTopkWaves];
-  uint32_t found[2];           // digit, count of keys above it
+  uint32_t wave_tot[kTopkWaves];
+  uint32_t found[3];   // digit, count above it, count in its bin
+  uint32_t n_cand, n_sel;
 };
 
 // Unsigned order of the key = rank order of the score.
@@ -37,58 +65,386 @@ __device__ __forceinline__ uint32_t score_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix sum of v over the workgroup (thread order); *total gets
-// the sum.  Ends with a barrier, so LDS it used may be reused at once.
-__device__ __forceinline__ uint32_t block_exclusive_sum(TopkSmem& sm, uint32_t v, uint32_t* total) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
-  if (lane == 63) sm.wave_sum[wid] = x;
-  __syncthreads();
-  uint32_t before = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kTopkWaves; ++w) {
-    const uint32_t c = sm.wave_sum[w];
-    before += w < wid ? c : 0;
-    tot += c;
-  }
-  __syncthreads();
-  *total = tot;
-  return before + x - v;
+// Every key is >= score_key(-inf) = 0x007fffff, so 0 is below every composite.
+__device__ __forceinline__ uint64_t composite(float x, int pos) {
+  return ((uint64_t)score_key(x) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)pos);
 }
 
-// The digit d of a histogram over nbins digits with
-// count(digits > d) < need <= count(digits >= d), and count(digits > d).
-__device__ __forceinline__ void find_digit(TopkSmem& sm, int nbins, uint32_t need, uint32_t* digit,
-                                           uint32_t* above) {
-  const int per = nbins / kTopkThreads;   // 2 or 1 bins per thread, highest digits first
-  const int t = threadIdx.x;
-  uint32_t v = 0;
-  for (int j = 0; j < per; ++j) v += sm.hist[nbins - 1 - (t * per + j)];
-  uint32_t total;
-  uint32_t run = block_exclusive_sum(sm, v, &total);
-  for (int j = 0; j < per; ++j) {
-    const int d = nbins - 1 - (t * per + j);
-    const uint32_t c = sm.hist[d];
-    if (run < need && need <= run + c) {
-      sm.found[0] = (uint32_t)d;
-      sm.found[1] = run;
+// Inclusive prefix sum of v over the wave's lanes: shifts within rows of
+// 16 lanes, then each row's total carried to the rows above it.
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x) {
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false);   // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false);   // row_bcast:31 into rows 2, 3
+  return x;
+}
+
+// The digit d of the histogram's 2^kW digits with count(digits > d) <
+// need <= count(digits >= d); count(digits > d) and count(digit d).
+// Thread t holds the t-th highest group of kPer digits (wave 0 the
+// highest); a prefix sum over the threads finds the group that crosses
+// `need`, its thread the digit.  Each thread zeroes its bins, so the next
+// level starts from a clear histogram.  need >= 1 and at most the
+// histogram's total.  Called by every thread, after a barrier that follows
+// the histogram's last update; ends with a barrier.
+template <int kW>
+__device__ __forceinline__ void find_digit(TopkSmem& sm, uint32_t need, uint32_t* digit, uint32_t* above,
+                                           uint32_t* in_bin) {
+  constexpr int kPer = (1 << kW) / kTopkThreads;   // 4 or 2
+  static_assert(kPer == 2 || kPer == 4, "digits per thread");
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int lo = (1 << kW) - kPer * (tid + 1);   // the thread's lowest digit
+  uint32_t h[kPer];
+  if constexpr (kPer == 4) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(&sm.hist[lo]);
+    h[0] = v[0], h[1] = v[1], h[2] = v[2], h[3] = v[3];
+    *reinterpret_cast<u32x4*>(&sm.hist[lo]) = u32x4{0u, 0u, 0u, 0u};
+  } else {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(&sm.hist[lo]);
+    h[0] = v[0], h[1] = v[1];
+    *reinterpret_cast<u32x2*>(&sm.hist[lo]) = u32x2{0u, 0u};
+  }
+  uint32_t s = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) s += h[j];
+  const uint32_t incl = wave_incl_sum(s);
+  if (lane == 63) sm.wave_tot[wid] = incl;
+  __syncthreads();
+  uint32_t run = incl - s;   // count of the digits above this thread's
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) run += w < wid ? sm.wave_tot[w] : 0u;
+  if (run < need && need <= run + s) {   // exactly one thread: walk its digits downwards
+#pragma unroll
+    for (int j = kPer - 1; j >= 0; --j) {
+      if (run < need && need <= run + h[j]) {
+        sm.found[0] = (uint32_t)(lo + j);
+        sm.found[1] = run;
+        sm.found[2] = h[j];
+      }
+      run += h[j];
     }
-    run += c;
   }
   __syncthreads();
   *digit = sm.found[0];
   *above = sm.found[1];
+  *in_bin = sm.found[2];
+}
+
+// hist[bin] += 1 for every active lane.  Lanes of one wave often share a
+// bin (scores cluster in a few exponents): up to four rounds add each
+// shared bin's count once, while the bins found are shared by more than
+// two lanes; the remaining lanes add singly.
+__device__ __forceinline__ void hist_add(TopkSmem& sm, uint32_t bin, bool active) {
+  const int lane = threadIdx.x & 63;
+  uint64_t todo = __ballot(active);
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    if (todo == 0) return;   // wave-uniform
+    const int leader = __builtin_ctzll(todo);
+    const uint32_t lb = __builtin_amdgcn_readlane(bin, leader);
+    const uint64_t same = __ballot(bin == lb) & todo;
+    const uint32_t c = (uint32_t)__popcll(same);
+    if (lane == leader) atomicAdd(&sm.hist[lb], c);
+    todo &= ~same;
+    if (c <= 2) break;   // wave-uniform
+  }
+  if ((todo >> lane) & 1) atomicAdd(&sm.hist[bin], 1u);
+}
+
+// First slot of this lane's `mine` appends: one LDS atomic per wave on
+// *count, lanes in order after it.
+__device__ __forceinline__ uint32_t wave_reserve(uint32_t* count, uint32_t mine) {
+  const uint32_t incl = wave_incl_sum(mine);
+  const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
+  uint32_t base = 0;
+  if (total != 0) {   // uniform
+    if ((threadIdx.x & 63) == 0) base = atomicAdd(count, total);
+    base = __builtin_amdgcn_readlane(base, 0);
+  }
+  return base + incl - mine;
+}
+
+// A row of L >= 1 positions: head [0, hh) before the first 16-byte
+// boundary, body of nv float4 vectors (positions hh + 4 j + e), tail
+// [hh + 4 nv, L).
+struct RowView {
+  const float* row;
+  const f32x4* body;
+  int L, hh, nv;
+};
+
+__device__ __forceinline__ RowView view_row(const float* row, int L) {
+  RowView rv;
+  rv.row = row;
+  rv.L = L;
+  rv.hh = min(L, (int)(((16u - (uint32_t)(reinterpret_cast<uintptr_t>(row) & 15u)) & 15u) >> 2));
+  rv.body = reinterpret_cast<const f32x4*>(row + rv.hh);
+  rv.nv = (L - rv.hh) >> 2;
+  return rv;
+}
+
+// f(valid, x, position) for the head's and the tail's positions, one per
+// thread; every lane makes the same calls.
+template <class F>
+__device__ __forceinline__ void for_singles(const RowView& rv, F&& f) {
+  const int tid = threadIdx.x;
+  if (rv.hh > 0) f(tid < rv.hh, rv.row[min(tid, rv.hh - 1)], tid);   // uniform
+  const int t0 = rv.hh + 4 * rv.nv;
+  if (t0 < rv.L) f(t0 + tid < rv.L, rv.row[min(t0 + tid, rv.L - 1)], t0 + tid);   // uniform
+}
+
+// Body vectors base + u * kTopkThreads + tid into x[u] (clamped to the last one); nv >= 1.
+template <int kN>
+__device__ __forceinline__ void load_batch(const RowView& rv, int base, f32x4 (&x)[kN]) {
+#pragma unroll
+  for (int u = 0; u < kN; ++u) x[u] = rv.body[min(base + u * kTopkThreads + (int)threadIdx.x, rv.nv - 1)];
+}
+
+// Appends composite(x) of the batch's positions with take(x, position) to
+// list[0 .. cap) (counted past cap, not stored), one LDS atomic per wave.
+// The takes are kept as one bit each between the count and the writes.
+template <class Take>
+__device__ __forceinline__ void emit_batch(const RowView& rv, const f32x4 (&x)[kUnroll], int base, Take&& take,
+                                           uint64_t* list, uint32_t* count, int cap) {
+  static_assert(4 * kUnroll <= 64, "one bit per position of a batch");
+  const int tid = threadIdx.x;
+  uint64_t m = 0;
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int j = base + u * kTopkThreads + tid;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m |= (j < rv.nv && take(x[u][e], rv.hh + 4 * j + e)) ? 1ull << (4 * u + e) : 0ull;
+  }
+  uint32_t slot = wave_reserve(count, (uint32_t)__popcll(m));
+  // each lane walks its set bits (few: the takes are sparse), two at a
+  // time, reading those scores again (the batch was just read: L2 hits)
+  while (__ballot(m != 0) != 0) {   // wave-uniform
+    const bool h0 = m != 0;
+    const int b0 = h0 ? __builtin_ctzll(m) : 0;
+    m &= m - 1;
+    const bool h1 = m != 0;
+    const int b1 = h1 ? __builtin_ctzll(m) : 0;
+    m &= m - 1;
+    const int p0 = rv.hh + 4 * (base + (b0 >> 2) * kTopkThreads + tid) + (b0 & 3);
+    const int p1 = rv.hh + 4 * (base + (b1 >> 2) * kTopkThreads + tid) + (b1 & 3);
+    const float x0 = rv.row[h0 ? p0 : 0];
+    const float x1 = rv.row[h1 ? p1 : 0];
+    if (h0) {
+      if (slot < (uint32_t)cap) list[slot] = composite(x0, p0);
+      ++slot;
+    }
+    if (h1) {
+      if (slot < (uint32_t)cap) list[slot] = composite(x1, p1);
+      ++slot;
+    }
+  }
+}
+
+// Appends composite(x) of every position of the row with take(x,
+// position), in no particular order.  x0 holds the body's first batch.
+template <class Take>
+__device__ __forceinline__ void compact_row(const RowView& rv, const f32x4 (&x0)[kUnroll], Take&& take,
+                                            uint64_t* list, uint32_t* count, int cap) {
+  constexpr int kStep = kUnroll * kTopkThreads;
+  if (rv.nv > 0) {
+    // two batches in flight: the next is requested before this one's appends
+    f32x4 xa[kUnroll], xb[kUnroll];
+    for (int u = 0; u < kUnroll; ++u) xa[u] = x0[u];
+    for (int base = 0; base < rv.nv; base += 2 * kStep) {
+      if (base + kStep < rv.nv) load_batch(rv, base + kStep, xb);   // uniform
+      emit_batch(rv, xa, base, take, list, count, cap);
+      if (base + kStep < rv.nv) {
+        if (base + 2 * kStep < rv.nv) load_batch(rv, base + 2 * kStep, xa);
+        emit_batch(rv, xb, base + kStep, take, list, count, cap);
+      }
+    }
+  }
+  for_singles(rv, [&](bool ok, float x, int pos) {
+    const bool t = ok && take(x, pos);
+    const uint32_t slot = wave_reserve(count, t ? 1u : 0u);
+    if (t && slot < (uint32_t)cap) list[slot] = composite(x, pos);
+  });
+}
+
+// f(valid, composite) over the row's positions; every lane makes the same
+// number of calls (f uses wave ballots).
+template <class F>
+__device__ __forceinline__ void sweep_row(const RowView& rv, F&& f) {
+  const int tid = threadIdx.x;
+  for (int base = 0; base < rv.nv; base += kSweepUnroll * kTopkThreads) {
+    f32x4 x[kSweepUnroll];
+    load_batch(rv, base, x);
+#pragma unroll
+    for (int u = 0; u < kSweepUnroll; ++u) {
+      const int j = base + u * kTopkThreads + tid;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f(j < rv.nv, composite(x[u][e], rv.hh + 4 * j + e));
+    }
+  }
+  for_singles(rv, [&](bool ok, float x, int pos) { f(ok, composite(x, pos)); });
+}
+
+// f(valid, composite) over the candidate list list[0 .. n), n >= 1, four
+// loads in flight per thread
+template <class F>
+__device__ __forceinline__ void sweep_list(const uint64_t* list, int n, F&& f) {
+  constexpr int kL = 4;
+  const int tid = threadIdx.x;
+  for (int base = 0; base < n; base += kL * kTopkThreads) {
+    uint64_t c[kL];
+#pragma unroll
+    for (int q = 0; q < kL; ++q) c[q] = list[min(base + q * kTopkThreads + tid, n - 1)];
+#pragma unroll
+    for (int q = 0; q < kL; ++q) f(base + q * kTopkThreads + tid < n, c[q]);
+  }
+}
+
+// Radix select over the composites a sweep visits: the largest threshold
+// Tc with count(composites >= Tc) >= need, using at most max_levels digits
+// (11, 11, 10, 11, 11, 10 bits from the top).  It stops early once `need`
+// takes a digit's bin whole, and then count(>= Tc) == need exactly; so it
+// does after six levels (the bin holds one composite).  With max_levels 2,
+// count(>= Tc) >= need and Tc is the lower edge of a 22-bit bin.  1 <= need
+// <= number of composites; the histogram is clear on entry and on exit.
+template <class Sweep>
+__device__ __forceinline__ uint64_t radix_threshold(TopkSmem& sm, uint32_t need, int max_levels, Sweep&& sweep) {
+  uint64_t prefix = 0;
+  int bits = 0;
+  for (int lvl = 0; lvl < max_levels; ++lvl) {
+    const int w = lvl % 3 == 2 ? 10 : 11;
+    const int shift = 64 - bits - w;
+    const uint32_t dmask = (1u << w) - 1;
+    sweep([&](bool ok, uint64_t c) {
+      const bool in = ok && ((c >> 1) >> (63 - bits)) == prefix;   // bits = 0: 0 == 0
+      hist_add(sm, (uint32_t)(c >> shift) & dmask, in);
+    });
+    __syncthreads();
+    uint32_t d, above, cnt;
+    if (w == 11)
+      find_digit<11>(sm, need, &d, &above, &cnt);
+    else
+      find_digit<10>(sm, need, &d, &above, &cnt);
+    need -= above;
+    prefix = (prefix << w) | d;
+    bits += w;
+    if (cnt == need) break;   // uniform
+  }
+  return prefix << (64 - bits);
+}
+
+// r for a sample of kSample out of L > kCand positions: about 3 k of the
+// row's composites lie at or above the sample's r-th largest.
+__device__ __forceinline__ uint32_t sample_rank(int L, int k) {
+  return (uint32_t)min(kSample, max(8, (int)((3ll * k * kSample + L - 1) / L)));
+}
+
+// Steps 1-3 for one row: the min(k, L) picks appended to sm.sel.
+__device__ __forceinline__ void select_row(TopkSmem& sm, const RowView& rv, int k) {
+  const int tid = threadIdx.x, L = rv.L;
+  // the body's first batch is requested before the sample's select runs
+  f32x4 x0[kUnroll];
+  if (rv.nv > 0) load_batch(rv, 0, x0);
+  if (L <= k) {   // every candidate is picked
+    compact_row(rv, x0, [](float, int) { return true; }, sm.sel, &sm.n_sel, kMaxTopk);
+    __syncthreads();
+    return;
+  }
+  if (L <= kCand) {   // the whole row is the list
+    compact_row(rv, x0, [](float, int) { return true; }, sm.cand, &sm.n_cand, kCand);
+  } else {
+    // 1. the sample: kSample positions spread over the row
+    const int sp = (int)(((int64_t)tid * L) / kSample);
+    const uint64_t sc = composite(rv.row[sp], sp);
+    const uint64_t t0 = radix_threshold(sm, sample_rank(L, k), 2, [&](auto&& f) { f(true, sc); });
+    // 2. the list: t0's low 42 bits are 0, so composite >= t0 is key >=
+    // kt.  Below key(-inf) every position qualifies (the list overflows:
+    // L > kCand).  Otherwise kt is the key of a float f0; when f0 is normal
+    // or infinite, key(x) >= kt is x >= f0 in float order (NaN is below f0
+    // on both sides, -0 equals +0, and a denormal x lies on the same side
+    // of f0 whether flushed or not).
+    const uint32_t kt = (uint32_t)(t0 >> 32);
+    const uint32_t fb = kt >= 0x80000000u ? kt ^ 0x80000000u : ~kt;
+    if (kt <= 0x007FFFFFu) {
+      if (tid == 0) sm.n_cand = (uint32_t)L;
+    } else if ((fb & 0x7F800000u) != 0) {
+      const float f0 = __uint_as_float(fb);
+      compact_row(rv, x0, [f0](float x, int) { return x >= f0; }, sm.cand, &sm.n_cand, kCand);
+    } else {
+      compact_row(rv, x0, [kt](float x, int) { return score_key(x) >= kt; }, sm.cand, &sm.n_cand, kCand);
+    }
+  }
+  __syncthreads();
+  const uint32_t nc = sm.n_cand;
+  // 3. select and collect
+  if (nc >= (uint32_t)k && nc <= (uint32_t)kCand) {
+    const uint64_t tc = radix_threshold(sm, (uint32_t)k, 6, [&](auto&& f) { sweep_list(sm.cand, (int)nc, f); });
+    sweep_list(sm.cand, (int)nc, [&](bool ok, uint64_t c) {
+      const bool take = ok && c >= tc;
+      const uint32_t slot = wave_reserve(&sm.n_sel, take ? 1u : 0u);
+      if (take && slot < (uint32_t)kMaxTopk) sm.sel[slot] = c;
+    });
+  } else {
+    const uint64_t tc = radix_threshold(sm, (uint32_t)k, 6, [&](auto&& f) { sweep_row(rv, f); });
+    if (rv.nv > 0) load_batch(rv, 0, x0);
+    compact_row(rv, x0, [tc](float x, int pos) { return composite(x, pos) >= tc; }, sm.sel, &sm.n_sel, kMaxTopk);
+  }
   __syncthreads();
 }
 
-__device__ __forceinline__ void clear_hist(TopkSmem& sm) {
-  for (int i = threadIdx.x; i < kBins; i += kTopkThreads) sm.hist[i] = 0;
-  __syncthreads();
+// v of lane (lane ^ kS), kS < 64, within the wave
+template <int kS>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+  if constexpr (kS == 1) {
+    return __builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1, 0, 3, 2]
+  } else if constexpr (kS == 2) {
+    return __builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2, 3, 0, 1]
+  } else if constexpr (kS == 4 || kS == 8) {
+    const uint32_t up = __builtin_amdgcn_update_dpp(0u, v, 0x100 + kS, 0xF, 0xF, false);   // row_shl: lane + kS
+    const uint32_t dn = __builtin_amdgcn_update_dpp(0u, v, 0x110 + kS, 0xF, 0xF, false);   // row_shr: lane - kS
+    return (threadIdx.x & kS) ? dn : up;
+  } else if constexpr (kS == 16) {
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (16 << 10));   // xor 16 within 32 lanes
+  } else {
+    return __shfl_xor(v, kS);
+  }
+}
+
+// One bitonic stage (kSize, kStride) over one composite per thread i:
+// pairs (i, i ^ kStride); segments of kSize alternate in direction so the
+// last stage leaves entries 0..511 descending.  Strides of 64 and more go
+// through LDS (buffer `buf`, one barrier), smaller ones stay in the wave.
+template <int kSize, int kStride>
+__device__ __forceinline__ void bitonic_stage(uint64_t& v, uint64_t* buf) {
+  const int i = threadIdx.x;
+  uint64_t o;
+  if constexpr (kStride >= 64) {
+    if (i < kMaxTopk) buf[i] = v;
+    __syncthreads();
+    o = i < kMaxTopk ? buf[i ^ kStride] : 0ull;
+  } else {
+    const uint32_t lo = lane_xor<kStride>((uint32_t)v);
+    const uint32_t hi = lane_xor<kStride>((uint32_t)(v >> 32));
+    o = ((uint64_t)hi << 32) | lo;
+  }
+  const bool keep_max = ((i & kStride) == 0) == ((i & kSize) == 0);
+  const uint64_t mx = v > o ? v : o, mn = v > o ? o : v;
+  v = keep_max ? mx : mn;
+}
+
+// Stages (kSize, kStride), (kSize, kStride / 2), .., then the next sizes up
+// to 512.  LDS stages alternate between two buffers, so each needs one
+// barrier: a buffer is written again only after a later barrier.
+template <int kSize, int kStride, int kLds>
+__device__ __forceinline__ void bitonic_from(uint64_t& v, uint64_t* buf0, uint64_t* buf1) {
+  bitonic_stage<kSize, kStride>(v, (kLds & 1) ? buf1 : buf0);
+  constexpr int kNext = kLds + (kStride >= 64 ? 1 : 0);
+  if constexpr (kStride > 1)
+    bitonic_from<kSize, kStride / 2, kNext>(v, buf0, buf1);
+  else if constexpr (kSize < kMaxTopk)
+    bitonic_from<kSize * 2, kSize, kNext>(v, buf0, buf1);
 }
 
 __global__ __launch_bounds__(kTopkThreads, 1) void mla_topk_kernel(const TopkParams p) {
@@ -100,74 +456,20 @@ __global__ __launch_bounds__(kTopkThreads, 1) void mla_topk_kernel(const TopkPar
   const int k = p.k;
   const int n = min(k, L);
 
-  // The threshold: keys above T are all taken, keys equal to T fill the
-  // remaining `eq_take` slots in position order.  With L <= k every
-  // candidate is taken.
-  const bool all = L <= k;
-  uint32_t T = 0, n_above = 0;
-  if (!all) {
-    clear_hist(sm);
-    for (int i = tid; i < L; i += kTopkThreads) atomicAdd(&sm.hist[score_key(row[i]) >> 21], 1u);
-    __syncthreads();
-    uint32_t d1, a1, d2, a2, d3, a3;
-    find_digit(sm, kBins, (uint32_t)k, &d1, &a1);
-    clear_hist(sm);
-    for (int i = tid; i < L; i += kTopkThreads) {
-      const uint32_t key = score_key(row[i]);
-      if ((key >> 21) == d1) atomicAdd(&sm.hist[(key >> 10) & 0x7FFu], 1u);
-    }
-    __syncthreads();
-    find_digit(sm, kBins, (uint32_t)k - a1, &d2, &a2);
-    clear_hist(sm);
-    const uint32_t hi = (d1 << 11) | d2;
-    for (int i = tid; i < L; i += kTopkThreads) {
-      const uint32_t key = score_key(row[i]);
-      if ((key >> 10) == hi) atomicAdd(&sm.hist[key & 0x3FFu], 1u);
-    }
-    __syncthreads();
-    find_digit(sm, 1024, (uint32_t)k - a1 - a2, &d3, &a3);
-    T = (hi << 10) | d3;
-    n_above = a1 + a2 + a3;
+  for (int i = tid; i < kBins; i += kTopkThreads) sm.hist[i] = 0;
+  if (tid == 0) {
+    sm.n_cand = 0;
+    sm.n_sel = 0;
   }
-  const uint32_t eq_take = (uint32_t)n - n_above;
-
-  // collect in position order
-  uint32_t cnt_above = 0, cnt_eq = 0;
-  for (int base = 0; base < L; base += kTopkThreads) {
-    const int i = base + tid;
-    const uint32_t key = i < L ? score_key(row[i]) : 0u;
-    const bool take_above = i < L && (all || key > T);
-    const bool is_eq = i < L && !all && key == T;
-    uint32_t total;
-    const uint32_t ex = block_exclusive_sum(sm, (take_above ? 1u : 0u) | (is_eq ? 0x10000u : 0u), &total);
-    const uint64_t comp = ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
-    if (take_above) sm.sel[cnt_above + (ex & 0xFFFFu)] = comp;
-    const uint32_t eq_rank = cnt_eq + (ex >> 16);
-    if (is_eq && eq_rank < eq_take) sm.sel[n_above + eq_rank] = comp;
-    cnt_above += total & 0xFFFFu;
-    cnt_eq += total >> 16;
-    if (!all && cnt_above >= n_above && cnt_eq >= eq_take) break;   // uniform: the rest is not taken
-  }
-  for (int i = n + tid; i < kMaxTopk; i += kTopkThreads) sm.sel[i] = 0;   // below every real pick
   __syncthreads();
+  if (L > 0) select_row(sm, view_row(row, L), k);
 
-  // bitonic sort, descending
-  for (int size = 2; size <= kMaxTopk; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      if (tid < kMaxTopk / 2) {
-        const int i = 2 * tid - (tid & (stride - 1)), j = i + stride;
-        const uint64_t a = sm.sel[i], c = sm.sel[j];
-        const bool desc = (i & size) == 0;
-        if ((a < c) == desc) {
-          sm.sel[i] = c;
-          sm.sel[j] = a;
-        }
-      }
-      __syncthreads();
-    }
-  }
-  for (int i = tid; i < k; i += kTopkThreads)
-    dst[i] = i < n ? (int32_t)(0xFFFFFFFFu - (uint32_t)(sm.sel[i] & 0xFFFFFFFFu)) : -1;
+  // 4. sort the n picks (exactly n were appended) descending, thread i
+  // holding entry i; entries past n hold 0, below every pick.  The
+  // candidate list is free by now and serves as the second LDS buffer.
+  uint64_t v = tid < n ? sm.sel[tid] : 0ull;
+  bitonic_from<2, 1, 0>(v, sm.cand, sm.sel);
+  if (tid < k) dst[tid] = tid < n ? (int32_t)(0xFFFFFFFFu - (uint32_t)(v & 0xFFFFFFFFu)) : -1;
 }
 
 }  // namespace

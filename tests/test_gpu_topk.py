@@ -95,3 +95,34 @@ def test_chained_before_the_decode_in_one_graph():
         assert np.array_equal(idx.cpu().numpy(), ref_idx), f"replay {rep}: topk_idx differs"
         check_attention(out, lse, ref_out, ref_lse, label=f"chained replay {rep}")
         torch.ones(1 << 20, device="cuda").sum()   # eager work between replays
+
+
+def test_unaligned_rows():
+    """Rows that start 4 bytes past a 16-byte boundary (a column slice of a
+    wider matrix): the scalar-load path."""
+    sc = G.indexer_scores(19, 5, 20001)
+    lens = [20000, 19999, 17000, 513, 3]
+    print("topk: unaligned rows", flush=True)
+    wide = torch.from_numpy(sc).cuda()
+    view = wide[:, 1:]
+    assert view.data_ptr() % 16 != 0
+    out = mlasd.mla_topk_select(view, torch.tensor(lens, dtype=torch.int32, device="cuda"), 512)
+    torch.cuda.synchronize()
+    ref = O.topk_select(np.ascontiguousarray(sc[:, 1:]), lens, 512)
+    assert np.array_equal(out.cpu().numpy(), ref)
+
+
+def test_threshold_guess_misses():
+    """Long rows where a guessed threshold from a spread-out sample leaves too
+    few or too many candidates: a constant row, a row whose large scores sit
+    only at every 64th position of its first 4,096, a row whose large scores
+    avoid those positions, and a row of 40,000 equal maxima."""
+    L = 65536
+    sc = np.zeros((4, L), dtype=np.float32)
+    sc[0] = 0.75
+    sc[1, : 64 * 64 : 64] = 10.0
+    sc[2] = -np.inf
+    sc[2, 1::64] = np.arange(1024, dtype=np.float32)
+    sc[3] = G.indexer_scores(20, 1, L)[0]
+    sc[3, :40000] = 5.0
+    _check(sc, [L, L, L, L], 512, "guess misses")
