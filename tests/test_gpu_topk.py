@@ -126,3 +126,11 @@ def test_threshold_guess_misses():
     sc[3] = G.indexer_scores(20, 1, L)[0]
     sc[3, :40000] = 5.0
     _check(sc, [L, L, L, L], 512, "guess misses")
+
+
+def test_rows_longer_than_a_batch_of_the_candidate_pass():
+    """Rows of up to 131,072 scores (the longest sequences of the
+    log-uniform workload): several load batches per row, and rows whose
+    length is not a multiple of 4."""
+    sc = G.indexer_scores(21, 6, 131072)
+    _check(sc, [131072, 131071, 98305, 65537, 16385, 16383], 512, "131072")
