@@ -240,6 +240,48 @@ def bench_topk(dev, stream, steps, batch=64, max_len=65536, k=512):
             "launch": f"HIP graph replay of {steps} calls"}
 
 
+def bench_chain(dev, wb, steps):
+    """Time top-k selection chained before the decode in one captured graph
+    on workload c3's cache: 64 rows of 65,536 fp32 scores -> topk_idx ->
+    decode, `steps` times, HIP events on the launch stream."""
+    import torch
+    import sparse_mla_decode_page_amd as mlasd
+    from gen.synth import indexer_scores
+    w = wb.w
+    sc = torch.from_numpy(indexer_scores(33, w.batch, int(w.seq_lens.max()))).to(dev)
+    idx = torch.empty((w.batch, w.topk), dtype=torch.int32, device=dev)
+    q = wb.dsets[0]["q"]
+    out = torch.empty((w.batch, 64, 448), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.batch, 64), dtype=torch.float32, device=dev)
+    stream = wb.stream
+
+    def step():
+        mlasd.mla_topk_select(sc, wb.lens, w.topk, out=idx, stream=stream)
+        mlasd.mla_sparse_decode(q, wb.kv, wb.pt, idx, wb.lens, w.softmax_scale, out=out, lse=lse, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            step()
+    stream.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(steps):
+            step()
+    with torch.cuda.stream(stream):
+        g.replay()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+    stream.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    del g
+    return {"workload": f"top-k of {w.batch} x {int(w.seq_lens.max())} fp32 scores (k={w.topk}), then the "
+                        f"decode of workload c3 on the selected entries",
+            "us_per_step": us, "launch": f"HIP graph replay of {steps} chained steps"}
+
+
 class Workbench:
     """One workload on the device: rotating input sets, the step function,
     and the graph of exactly `steps` steps."""
@@ -517,6 +559,7 @@ def main():
         if key == "config3" and not args.no_append:
             per["kv_append"] = bench_append(dev, wb.kv, wb.pt, int(w.seq_lens.min()), 50, wb.stream)
             per["topk_select"] = bench_topk(dev, wb.stream, 50)
+            per["topk_then_decode"] = bench_chain(dev, wb, 50)
         if key != head_key:
             del wb
             torch.cuda.empty_cache()
