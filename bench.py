@@ -476,7 +476,8 @@ def main():
     ap.add_argument("--no-append", action="store_true", help="skip the cache-append measurement")
     ap.add_argument("--op", choices=["decode", "append", "topk"], default="decode",
                     help="append: time only the cache-append kernel (on workload c3's pool); "
-                         "topk: time only the top-k selection (64 x 65,536 scores)")
+                         "topk: time only the top-k selection (--batch rows, default 64, of "
+                         "--seq-len scores, default 65,536; k = --topk)")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the flushed single-call timing and the copy ceiling (profiling runs)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -523,7 +524,8 @@ def main():
         print(json.dumps(res), flush=True)
         return
     if args.op == "topk":
-        res = bench_topk(dev, torch.cuda.Stream(dev), args.steps)
+        res = bench_topk(dev, torch.cuda.Stream(dev), args.steps, batch=args.batch or 64,
+                         max_len=args.seq_len, k=args.topk)
         res["metric"] = "top-k selection: query rows/s"
         print(json.dumps(res), flush=True)
         return

@@ -11,7 +11,7 @@
 // unsigned order is the score order: composites are distinct and their
 // unsigned order is the rank order, so the picks are exactly the min(k, L)
 // largest composites.
-//   1. Threshold guess (rows over kCand positions): the composites of 512
+//   1. Threshold guess (rows over kSmallRow positions): the composites of 512
 //      positions spread over the row; t0, the lower edge of the 22-bit bin
 //      holding their r-th largest, r set so about 3 k of the row's
 //      composites lie at or above t0.
@@ -44,6 +44,7 @@ constexpr int kTopkThreads = 512;
 constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kBins = 2048;
 constexpr int kCand = 16384;       // LDS candidate list (128 KiB)
+constexpr int kSmallRow = 4096;    // rows up to this length go to the list whole
 constexpr int kSample = kTopkThreads;
 constexpr int kUnroll = 8;         // float4 loads in flight per thread in a compaction pass
 constexpr int kSweepUnroll = 2;    // and in a histogram pass over the row (the rare path)
@@ -335,7 +336,7 @@ __device__ __forceinline__ uint64_t radix_threshold(TopkSmem& sm, uint32_t need,
   return prefix << (64 - bits);
 }
 
-// r for a sample of kSample out of L > kCand positions: about 3 k of the
+// r for a sample of kSample out of L > kSmallRow positions: about 3 k of the
 // row's composites lie at or above the sample's r-th largest.
 __device__ __forceinline__ uint32_t sample_rank(int L, int k) {
   return (uint32_t)min(kSample, max(8, (int)((3ll * k * kSample + L - 1) / L)));
@@ -352,7 +353,7 @@ __device__ __forceinline__ void select_row(TopkSmem& sm, const RowView& rv, int 
     __syncthreads();
     return;
   }
-  if (L <= kCand) {   // the whole row is the list
+  if (L <= kSmallRow) {   // the whole row is the list
     compact_row(rv, x0, [](float, int) { return true; }, sm.cand, &sm.n_cand, kCand);
   } else {
     // 1. the sample: kSample positions spread over the row
@@ -360,15 +361,18 @@ __device__ __forceinline__ void select_row(TopkSmem& sm, const RowView& rv, int 
     const uint64_t sc = composite(rv.row[sp], sp);
     const uint64_t t0 = radix_threshold(sm, sample_rank(L, k), 2, [&](auto&& f) { f(true, sc); });
     // 2. the list: t0's low 42 bits are 0, so composite >= t0 is key >=
-    // kt.  Below key(-inf) every position qualifies (the list overflows:
-    // L > kCand).  Otherwise kt is the key of a float f0; when f0 is normal
+    // kt.  Below key(-inf) every position qualifies: the whole row is the
+    // list, or overflows it.  Otherwise kt is the key of a float f0; when f0 is normal
     // or infinite, key(x) >= kt is x >= f0 in float order (NaN is below f0
     // on both sides, -0 equals +0, and a denormal x lies on the same side
     // of f0 whether flushed or not).
     const uint32_t kt = (uint32_t)(t0 >> 32);
     const uint32_t fb = kt >= 0x80000000u ? kt ^ 0x80000000u : ~kt;
     if (kt <= 0x007FFFFFu) {
-      if (tid == 0) sm.n_cand = (uint32_t)L;
+      if (L <= kCand)
+        compact_row(rv, x0, [](float, int) { return true; }, sm.cand, &sm.n_cand, kCand);
+      else if (tid == 0)
+        sm.n_cand = (uint32_t)L;
     } else if ((fb & 0x7F800000u) != 0) {
       const float f0 = __uint_as_float(fb);
       compact_row(rv, x0, [f0](float x, int) { return x >= f0; }, sm.cand, &sm.n_cand, kCand);

@@ -134,3 +134,17 @@ def test_rows_longer_than_a_batch_of_the_candidate_pass():
     length is not a multiple of 4."""
     sc = G.indexer_scores(21, 6, 131072)
     _check(sc, [131072, 131071, 98305, 65537, 16385, 16383], 512, "131072")
+
+
+def test_mid_length_rows_whose_guess_takes_everything():
+    """Rows of 4,097 .. 16,384 scores take the sampled threshold; when the
+    sample's threshold is -inf (rows of -inf or NaN) every position is a
+    candidate and the whole row becomes the list."""
+    L = 8000
+    sc = np.zeros((4, L), dtype=np.float32)
+    sc[0] = -np.inf
+    sc[1] = np.nan
+    sc[2] = -np.inf
+    sc[2, 7000:7300] = 1.0
+    sc[3] = G.indexer_scores(22, 1, L)[0]
+    _check(sc, [L, L, L, 5000], 512, "mid-length guesses")
