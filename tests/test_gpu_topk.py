@@ -148,3 +148,20 @@ def test_mid_length_rows_whose_guess_takes_everything():
     sc[2, 7000:7300] = 1.0
     sc[3] = G.indexer_scores(22, 1, L)[0]
     _check(sc, [L, L, L, 5000], 512, "mid-length guesses")
+
+
+def test_threshold_at_zero_or_denormal_scores():
+    """Long rows where the guessed threshold lands on a zero or denormal
+    score, so candidates are tested by key instead of by float compare:
+    mostly +-0 with a few positives, denormals of both signs, and a mix."""
+    L = 20000
+    rng = np.random.default_rng(23)
+    sc = np.zeros((3, L), dtype=np.float32)
+    sc[0] = np.where(rng.random(L) < 0.5, np.float32(0.0), np.float32(-0.0))
+    sc[0, rng.choice(L, 100, replace=False)] = rng.random(100).astype(np.float32) + 1.0
+    tiny = np.float32(1e-42)   # a denormal
+    sc[1] = (rng.integers(-3, 4, L) * tiny).astype(np.float32)
+    sc[2] = np.where(rng.random(L) < 0.3, (rng.integers(-2, 3, L) * tiny).astype(np.float32),
+                     rng.standard_normal(L).astype(np.float32) - 4.0)
+    assert np.any(np.abs(sc[1]) > 0) and np.all(np.abs(sc[1]) < 1e-37)
+    _check(sc, [L, L, L], 512, "zero / denormal thresholds")
