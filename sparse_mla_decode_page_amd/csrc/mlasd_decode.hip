@@ -20,7 +20,9 @@
 //       the 448 nope dims, bf16 over the 64 rope dims) and, between those
 //       MFMAs, the online softmax of tile t - 1 in fp32 (exp2 domain),
 //       handing the fp16 P^T operand and the accumulator rescale factor to
-//       their PV waves through LDS;
+//       their PV waves through LDS.  In the 32-head kernel a second wave
+//       takes nope dims [192, 448) of the scores and hands its fp32 part
+//       over through LDS; the QK wave adds it one stage later;
 //   PV waves (two per QK wave, 224 output dims each) accumulate
 //       O^T[dims][heads] += V^T P^T of tile t - 2 on v_mfma_f32_32x32x16_f16,
 //       the V^T operand read from the token-major tile by
@@ -79,6 +81,7 @@ constexpr float kRescaleLog2 = 8.f;       // lazy-rescale threshold: P <= 2^8
 constexpr int kQRowH = 520;               // Q staging row (16-bit units): 512 + 8 pad
 constexpr int kStageRowB = 464;           // epilogue staging row: 224 bf16 (448 B) + 16 B
 constexpr int kNoRebase = -100000;        // R before any tile
+constexpr int kQkSplit = 12;              // 32-head kernel: nope k-steps of the QK wave; wave 7 takes the rest
 
 struct __align__(16) Smem {
   uint16_t kv[kBufs][kTileTokens * kRowH];   // 4 x 32 KiB tile buffers
@@ -94,6 +97,7 @@ struct __align__(16) Smem {
   uint16_t tok_entry[kMaxTopk];           //                 entry index in the slice
   int32_t wave_cnt[kWaves];
   alignas(16) float sf[4][16][8];        // [producer][token][group]: 2^(k_g - r_t) of the share's tokens
+  f32x4 sx[2][4][64];                     // [tile & 1][register quad][lane]: 32-head kernel, wave 7's partial scores
 };
 static_assert(kHeads * kQRowH * 2 <= 3 * kTileTokens * kRowB, "q staging must fit tile buffers 1-3");
 static_assert(4 * 32 * kStageRowB <= 2 * kTileTokens * kRowB, "epilogue staging must fit two tile buffers");
@@ -394,9 +398,12 @@ __device__ __forceinline__ void stage_q(Smem& sm, const QChunk& q, int hl, int c
 // QK waves
 // ---------------------------------------------------------------------------
 
+// Q^T operands of a wave: nope k-steps [kA, kB) and, if kRope, the 4 rope
+// k-steps.
+template <int kA, int kB, bool kRope>
 struct QRegs {
-  f16x8 n[kNopeSteps];
-  bf16x8 r[4];
+  f16x8 n[kB - kA];
+  bf16x8 r[kRope ? 4 : 1];
 };
 
 // Rebase exponent of tile row 8 (i / 4) + 4 half + i % 4 (the row a QK
@@ -451,55 +458,67 @@ __device__ __forceinline__ void softmax_piece(int k, Softmax& st, const f32x16& 
   }
 }
 
-// One QK-wave stage: S^T[token][head] for the tile row at krow (k-step k
-// reads chunk 2 k + l / 32, at krow + koff[k % 8] + 128 (k / 8)) into acc;
-// in a tile with rebased rows (flag word `tflag` nonzero) the nope part of
-// row r is multiplied by 2^r_t (exact in fp32; exponents from `rt`) before
-// the rope k-steps are added.  kSM: also the softmax of the previous tile
-// (scores in prev), cut into pieces issued between the nope MFMAs so the
-// VALU work runs while the matrix core is busy.  Scheduling barriers keep
-// each k-step's read (kQkAhead steps ahead), MFMA and piece together.
-template <bool kSM, int kProd>
-__device__ __forceinline__ void qk_stage(const uint16_t* krow, const int* koff, const QRegs& q, f32x16& acc,
-                                         const int32_t* tflags, const int8_t* rt, int half,
+// One QK-wave stage: S^T[token][head] for the tile row at krow over nope
+// k-steps [kA, kB) and, if kRope, the 4 rope k-steps (k-step k reads chunk
+// 2 k + l / 32, at krow + koff[k % 8] + 128 (k / 8)) into acc; in a tile
+// with rebased rows (flag word `tflag` nonzero) the nope part of row r is
+// multiplied by 2^r_t (exact in fp32; exponents from `rt`) before the rope
+// k-steps are added.  kSM: also the softmax of the previous tile (scores in
+// prev), cut into pieces issued between the MFMAs so the VALU work runs
+// while the matrix core is busy.  Scheduling barriers keep each k-step's
+// read (kQkAhead steps ahead), MFMA and piece together.
+template <bool kSM, int kProd, int kA, int kB, bool kRope>
+__device__ __forceinline__ void qk_stage(const uint16_t* krow, const int* koff, const QRegs<kA, kB, kRope>& q,
+                                         f32x16& acc, const int32_t* tflags, const int8_t* rt, int half,
                                          const f32x16& prev, float c_h, float& m_run, float& l_run, float& alpha,
                                          u32x4* pk) {
   constexpr int kRing = kQkAhead + 1;
+  constexpr int kNn = kB - kA;                      // nope k-steps
+  constexpr int kSteps = kNn + (kRope ? 4 : 0);
+  auto kread = [&](int j) {
+    const int k = j < kNn ? kA + j : kNopeSteps + (j - kNn);   // the j-th k-step
+    return *(const u32x4*)(krow + koff[k & 7] + 128 * (k >> 3));
+  };
   const i32x4 fl = *(const i32x4*)tflags;   // consumed after the nope steps
+  auto rebase_rows = [&]() {
+    const int tf = kProd == 2 ? fl.x | fl.y : fl.x | fl.y | fl.z | fl.w;
+    if (__builtin_amdgcn_readfirstlane(tf) != 0) {   // rare
+      const u32x4 rr0 = *(const u32x4*)rt;
+      const u32x4 rr1 = *(const u32x4*)(rt + 16);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = __builtin_ldexpf(acc[i], row_rebase(rr0, rr1, i, half));
+    }
+  };
   u32x4 ka[kRing];
 #pragma unroll
-  for (int k = 0; k < kQkAhead; ++k) ka[k] = *(const u32x4*)(krow + koff[k & 7] + 128 * (k >> 3));
+  for (int j = 0; j < kQkAhead; ++j) ka[j] = kread(j);
   acc = f32x16{};
   Softmax st{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int k = 0; k < kNopeSteps; ++k) {
-    ka[(k + kQkAhead) % kRing] = *(const u32x4*)(krow + koff[(k + kQkAhead) & 7] + 128 * ((k + kQkAhead) >> 3));
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, ka[k % kRing]), q.n[k], acc, 0, 0, 0);
+  for (int j = 0; j < kSteps; ++j) {
+    if (j + kQkAhead < kSteps) ka[(j + kQkAhead) % kRing] = kread(j + kQkAhead);
+    if (j == kNn) rebase_rows();
+    if (j < kNn)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, ka[j % kRing]), q.n[j], acc, 0, 0, 0);
+    else
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[j % kRing]), q.r[j - kNn], acc,
+                                                    0, 0, 0);
     if constexpr (kSM) {
-      if (k <= 18) {
-        softmax_piece(k, st, prev, c_h, m_run, l_run, alpha, pk);
+      if (j <= 18) {
+        softmax_piece(j, st, prev, c_h, m_run, l_run, alpha, pk);
         // keep the piece here (the compiler would sink it to its use)
-        if (k == 1) asm volatile("" ::"v"(alpha), "v"(st.m_new));
-        if (k >= 2 && k < 18) asm volatile("" ::"v"(st.sum), "v"(st.e_even), "v"(pk[(k - 2) >> 3][((k - 2) >> 1) & 3]));
-        if (k == 18) asm volatile("" ::"v"(l_run));
+        if (j == 1) asm volatile("" ::"v"(alpha), "v"(st.m_new));
+        if (j >= 2 && j < 18) asm volatile("" ::"v"(st.sum), "v"(st.e_even), "v"(pk[(j - 2) >> 3][((j - 2) >> 1) & 3]));
+        if (j == 18) asm volatile("" ::"v"(l_run));
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
+    if (j < kNn || (kSM && j <= 18)) __builtin_amdgcn_sched_barrier(0);
   }
-  const int tf = kProd == 2 ? fl.x | fl.y : fl.x | fl.y | fl.z | fl.w;
-  if (__builtin_amdgcn_readfirstlane(tf) != 0) {   // rare
-    const u32x4 rr0 = *(const u32x4*)rt;
-    const u32x4 rr1 = *(const u32x4*)(rt + 16);
+  if constexpr (kSM) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = __builtin_ldexpf(acc[i], row_rebase(rr0, rr1, i, half));
+    for (int j = kSteps; j <= 18; ++j) softmax_piece(j, st, prev, c_h, m_run, l_run, alpha, pk);
   }
-#pragma unroll
-  for (int k = kNopeSteps; k < 32; ++k) {
-    if (k + kQkAhead < 32)
-      ka[(k + kQkAhead) % kRing] = *(const u32x4*)(krow + koff[(k + kQkAhead) & 7] + 128 * ((k + kQkAhead) >> 3));
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[k % kRing]), q.r[k - kNopeSteps], acc,
-                                                  0, 0, 0);
-  }
+  if constexpr (!kRope) rebase_rows();
 }
 
 // ---------------------------------------------------------------------------
@@ -600,8 +619,9 @@ __device__ __forceinline__ void store_pv(const DecodeParams& p, uint8_t* stage, 
 // waves 0 and 1 (SIMDs 0, 1), producers 2 and 3 (16 tokens each, SIMDs 2,
 // 3), PV waves 4, 6 (heads 0-31, dims 0-223 / 224-447) and 5, 7 (heads
 // 32-63): each SIMD runs one MFMA-heavy wave and one lighter one.
-// kHG = 2: 32 heads: QK wave 0, PV waves 2 and 3, producers 1, 4, 5, 6 (8
-// tokens each), wave 7 spare.
+// kHG = 2: 32 heads: QK wave 0 (nope dims [0, 192) and rope), second QK
+// wave 7 (nope dims [192, 448)), PV waves 2 and 3, producers 1, 4, 5, 6 (8
+// tokens each).
 //
 // Stage t (between barriers B_t and B_t+1, t = 0..ntiles): producers
 // dequantise tile t + 1, QK waves compute the scores of tile t and the
@@ -653,7 +673,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
   const int ntiles = (n_valid + kTileTokens - 1) / kTileTokens;
   const int nstages = ntiles > 0 ? ntiles + 2 : 0;   // barriers B_0 .. B_ntiles+1
 
-  // 0 QK, 1 PV, 2 producer, 3 spare
+  // 0 QK, 1 PV, 2 producer, 3 second QK wave (32-head kernel)
   const int role = kHG == 1 ? (wid < 2 ? 0 : (wid == 2 || wid == 3) ? 2 : 1)
                             : (wid == 0 ? 0 : (wid == 2 || wid == 3) ? 1 : wid == 7 ? 3 : 2);
   const int pw = kHG == 1 ? wid - 2 : (wid == 1 ? 0 : wid - 3);   // producer index
@@ -710,8 +730,33 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
     return;
   }
 
-  if (role == 3) {   // spare wave: only passes the barriers
-    for (int t = 0; t < nstages; ++t) __syncthreads();
+  if (role == 3) {
+    // 32-head kernel, wave 7: the nope k-steps [kQkSplit, 28) of each tile's
+    // scores, handed to the QK wave through LDS (it adds them one stage later)
+    const int col = lane & 31, half = lane >> 5;
+    QRegs<kQkSplit, kNopeSteps, false> q;
+    {
+      const uint16_t* qs = reinterpret_cast<const uint16_t*>(&sm.kv[1][0]) + col * kQRowH + 8 * half;
+#pragma unroll
+      for (int k = kQkSplit; k < kNopeSteps; ++k) q.n[k - kQkSplit] = *(const f16x8*)(qs + 16 * k);
+    }
+    int koff[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) koff[j] = kChunkH * chunk_at(col, 2 * j + half);
+    __syncthreads();   // B_0
+    f32x16 acc;
+    float m_unused = 0.f, l_unused = 0.f, a_unused = 1.f;
+    for (int t = 0; t + 1 < nstages; ++t) {
+      if (t < ntiles) {
+        const int buf = t % kBufs;
+        qk_stage<false, kProd, kQkSplit, kNopeSteps, false>(&sm.kv[buf][col * kRowH], koff, q, acc, sm.tflag[buf],
+                                                             sm.rt[buf], half, acc, 0.f, m_unused, l_unused,
+                                                             a_unused, nullptr);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) sm.sx[t & 1][c][lane] = f32x4{acc[4 * c], acc[4 * c + 1], acc[4 * c + 2], acc[4 * c + 3]};
+      }
+      __syncthreads();   // B_{t+1}
+    }
     return;
   }
 
@@ -764,11 +809,12 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
   const int qk = kHG == 1 ? wid : 0;
   const int col = lane & 31, half = lane >> 5;
   const int hl = 32 * qk + col;                      // head within the workgroup
-  QRegs q;
+  constexpr int kQkN = kHG == 2 ? kQkSplit : kNopeSteps;   // nope k-steps of this wave
+  QRegs<0, kQkN, true> q;
   {
     const uint16_t* qs = reinterpret_cast<const uint16_t*>(&sm.kv[1][0]) + hl * kQRowH + 8 * half;
 #pragma unroll
-    for (int k = 0; k < kNopeSteps; ++k) q.n[k] = *(const f16x8*)(qs + 16 * k);
+    for (int k = 0; k < kQkN; ++k) q.n[k] = *(const f16x8*)(qs + 16 * k);
 #pragma unroll
     for (int k = 0; k < 4; ++k) q.r[k] = *(const bf16x8*)(qs + kDNope + 16 * k);
   }
@@ -790,10 +836,22 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
     const i32x4 pr = *(const i32x4*)sm.rmax[pbuf];
     float alpha = 1.f;
     u32x4 pk[2];
+    if constexpr (kHG == 2) {
+      if (t > 0) {   // wave 7's part of the previous tile's scores
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const f32x4 x = sm.sx[(t - 1) & 1][c][lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) prev[4 * c + e] += x[e];
+        }
+      }
+    }
     if (t == 0) {
-      qk_stage<false, kProd>(krow, koff, q, cur, sm.tflag[buf], sm.rt[buf], half, prev, c_h, m_run, l_run, alpha, pk);
+      qk_stage<false, kProd, 0, kQkN, true>(krow, koff, q, cur, sm.tflag[buf], sm.rt[buf], half, prev, c_h, m_run,
+                                            l_run, alpha, pk);
     } else if (t < ntiles) {
-      qk_stage<true, kProd>(krow, koff, q, cur, sm.tflag[buf], sm.rt[buf], half, prev, c_h, m_run, l_run, alpha, pk);
+      qk_stage<true, kProd, 0, kQkN, true>(krow, koff, q, cur, sm.tflag[buf], sm.rt[buf], half, prev, c_h, m_run,
+                                           l_run, alpha, pk);
     } else {
       // the last tile, possibly partial: scaled here, rows past the end -inf
       const int tile_valid = n_valid - (t - 1) * kTileTokens;

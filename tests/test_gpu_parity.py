@@ -172,19 +172,39 @@ def test_decode_forced_split(i, nsplit):
     check_attention(out, lse, ref_out, ref_lse, label=f"config {i} nsplit={nsplit}")
 
 
+def _groupings_agree(r64, r32, label):
+    """The 64-head and 32-head kernels run the same tiles in the same order.
+    They differ in one place: the 32-head kernel splits each score's 512-dim
+    dot product over two waves (nope dims [0, 192) plus rope, then
+    [192, 448)) and adds the two fp32 parts, where the 64-head kernel sums it
+    in one chain.  That rounding shows as lse within 1e-5 (relative) and out
+    within 1 % of each query's largest |out| (measured: 4e-6 and 0.54 % at
+    most over c0-c4, with 0.02-0.4 % of out elements different at all)."""
+    (o1, l1), (o2, l2) = r64, r32
+    fin = torch.isfinite(l1)
+    assert torch.equal(fin, torch.isfinite(l2)), label
+    assert torch.equal(l1[~fin], l2[~fin]), label
+    if fin.any():
+        dl = (l1[fin] - l2[fin]).abs()
+        assert (dl <= 1e-5 * l1[fin].abs().clamp_min(1.0)).all(), f"{label}: lse {dl.max().item():.3g}"
+    a, b = o1.float(), o2.float()
+    mq = torch.maximum(a.abs(), b.abs()).amax(dim=(1, 2), keepdim=True)
+    assert ((a - b).abs() <= 1e-2 * mq).all(), label
+
+
 @pytest.mark.parametrize("i,nsplit", [(0, 1), (1, 1), (1, 8), (2, 4), (2, 8), (3, 2), (3, 1), (4, 1)])
-def test_head_groups_bitwise_equal(i, nsplit):
-    """Two 32-head workgroups per slice compute exactly what one 64-head
-    workgroup computes: the same tiles in the same order with the same
-    instructions per head, so the results agree bit for bit."""
+def test_head_groups_agree(i, nsplit):
+    """Two 32-head workgroups per slice against one 64-head workgroup: both
+    meet the oracle bar, and they agree to the rounding of the scores'
+    summation order."""
     w, (ref_out, ref_lse) = config(i)
     print(f"head groups config {i} nsplit={nsplit}", flush=True)
     d = to_device(w)
     r = [decode(d, w.softmax_scale, nsplit=nsplit, head_groups=hg) for hg in (1, 2)]
     torch.cuda.synchronize()
-    for o, l in r[1:]:
-        assert torch.equal(r[0][0], o) and torch.equal(r[0][1], l)
-    check_attention(r[1][0], r[1][1], ref_out, ref_lse, label=f"config {i} nsplit={nsplit} 32-head groups")
+    _groupings_agree(r[0], r[1], f"config {i} nsplit={nsplit}")
+    for hg, (o, l) in zip((1, 2), r):
+        check_attention(o, l, ref_out, ref_lse, label=f"config {i} nsplit={nsplit} {64 // hg}-head groups")
 
 
 def _custom(seed, lens, topk, **kw):
@@ -330,7 +350,7 @@ def test_rebased_and_plain_tiles_mixed():
     a power-of-two rebase (tiny groups near 1e-9, large ones near 1e6), in
     both orders, so the running reference rises, stays and multiplies O
     back: the oracle bar (max-norm form: values up to 1e6) holds and 32/64-head
-    workgroups agree bit for bit."""
+    workgroups agree to the rounding of the scores' summation order."""
     def gs(rng, n):
         kind = rng.integers(0, 3, n)
         scale = np.where(kind == 0, 1.0, np.where(kind == 1, 1e-9, 1e6))
@@ -342,7 +362,7 @@ def test_rebased_and_plain_tiles_mixed():
     d = to_device(w)
     r = [decode(d, w.softmax_scale, nsplit=1, head_groups=hg) for hg in (1, 2)]
     torch.cuda.synchronize()
-    assert torch.equal(r[0][0], r[1][0]) and torch.equal(r[0][1], r[1][1])
+    _groupings_agree(r[0], r[1], "mixed rebased tiles")
     for ns in (None, 1, 2):
         _check_custom(w, nsplit=ns, label=f"mixed rebased tiles nsplit={ns}", maxnorm=True)
 
