@@ -369,27 +369,33 @@ __device__ __forceinline__ void stage_q(Smem& sm, const QChunk& q, int hl, int c
         mx = max(mx, max(w & 0x7FFFu, (w >> 16) & 0x7FFFu));
       }
   }
-  mx = max(mx, (uint32_t)__shfl_xor((int)mx, 1));
-  mx = max(mx, (uint32_t)__shfl_xor((int)mx, 2));
-  mx = max(mx, (uint32_t)__shfl_xor((int)mx, 4));
+  // max over the head's 8 lanes: xor 1 and xor 2 (quad permutes), then
+  // each lane with its mirror in the 8-lane half row (the other quad)
+  mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0xB1, 0xF, 0xF, false));
+  mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x4E, 0xF, 0xF, false));
+  mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x141, 0xF, 0xF, false));
   const int E = (int)(mx >> 7) - 127;
   const int eh = mx == 0 ? 0 : min(max(E - 15, -100), 100);
   // 2^-e_h, negated for a negative softmax scale (the scores change sign,
   // the exp2-domain factor c_h stays >= 0)
   const float down = __uint_as_float(((uint32_t)(127 - eh) << 23) | (neg ? 0x80000000u : 0u));
   uint16_t* dst = reinterpret_cast<uint16_t*>(&sm.kv[1][0]) + hl * kQRowH + 64 * chunk;
+  auto convert = [&](auto cvt2) {   // one branch per thread: a thread's 64 dims are all nope or all rope
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    u32x4 o;
+    for (int i = 0; i < 8; ++i) {
+      u32x4 o;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t w = q.v[i][k];
-      const float f0 = __uint_as_float(w << 16) * down;
-      const float f1 = __uint_as_float(w & 0xffff0000u) * down;
-      o[k] = chunk < 7 ? pack2(__builtin_amdgcn_cvt_pkrtz(f0, f1)) : bf16x2_rne(f0, f1);
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t w = q.v[i][k];
+        o[k] = cvt2(__uint_as_float(w << 16) * down, __uint_as_float(w & 0xffff0000u) * down);
+      }
+      *(u32x4*)(dst + 8 * i) = o;
     }
-    *(u32x4*)(dst + 8 * i) = o;
-  }
+  };
+  if (chunk < 7)
+    convert([](float f0, float f1) { return pack2(__builtin_amdgcn_cvt_pkrtz(f0, f1)); });
+  else
+    convert([](float f0, float f1) { return bf16x2_rne(f0, f1); });
   if (chunk == 0) sm.eh[hl] = eh;
   (void)lane;
 }
@@ -662,7 +668,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
   const int q_hl = tid >> 3, q_chunk = tid & 7;   // q staging: 8 threads per head
   const bool q_thread = q_hl < kHeadsWG;
   QChunk qc;
-  load_q(qc, p, b, head_base + (q_hl & (kHeadsWG - 1)), q_chunk);   // threads past the group reload its heads
+  // every thread of the 64-head kernel loads q; in the 32-head kernel the
+  // waves past the group's heads skip it (wave-uniform)
+  if (kHG == 1 || q_thread) load_q(qc, p, b, head_base + (q_hl & (kHeadsWG - 1)), q_chunk);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < 4; ++j) pt_lds[j * kThreads + tid] = ptv[j];   // entries past n_staged are never read
