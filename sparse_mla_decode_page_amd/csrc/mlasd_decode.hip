@@ -232,7 +232,10 @@ struct Share {
 
 // Loads of a share.  Entries past the last valid one re-read the slice's
 // last valid record (already cached); their scores are masked.  n_valid >= 1.
-template <int kTok>
+// !kWide (the pool lies within 4 GiB of kv): each address is kv plus a
+// zero-extended 32-bit offset, which the loads take as an SGPR base and a
+// VGPR offset, with no 64-bit address arithmetic per load.
+template <int kTok, bool kWide>
 __device__ __forceinline__ void load_share(Share<kTok>& r, const Smem& sm, const uint8_t* kv, int list0, int n_valid,
                                            int lane) {
   const int p = lane & 31;
@@ -246,11 +249,17 @@ __device__ __forceinline__ void load_share(Share<kTok>& r, const Smem& sm, const
   for (int h = 0; h < kTok / 2; ++h) {
     const int e = list0 + 2 * h + (lane >> 5);
     const u64x2 a = sm.tok[full ? e : min(e, n_valid - 1)];
-    const uint8_t* rec = kv + a.x;
-    r.b[h].n0 = *(const u32x2*)(rec + 8 * p);
-    r.b[h].n1 = *(const u32x4*)(rec + off1);
+    if constexpr (kWide) {
+      const uint8_t* rec = kv + a.x;
+      r.b[h].n0 = *(const u32x2*)(rec + 8 * p);
+      r.b[h].n1 = *(const u32x4*)(rec + off1);
+    } else {
+      const uint32_t o = (uint32_t)a.x;
+      r.b[h].n0 = *(const u32x2*)(kv + (uint32_t)(o + 8 * p));
+      r.b[h].n1 = *(const u32x4*)(kv + (uint32_t)(o + off1));
+    }
   }
-  r.sc = *(const u32x2*)(kv + a_sc.y);
+  r.sc = *(const u32x2*)(kv + (kWide ? a_sc.y : (uint64_t)(uint32_t)a_sc.y));
 }
 
 // Lane byte offsets, from the share's first row, of the 16-byte chunk p of
@@ -633,7 +642,7 @@ __device__ __forceinline__ void store_pv(const DecodeParams& p, uint8_t* stage, 
 // dequantise tile t + 1, QK waves compute the scores of tile t and the
 // softmax of tile t - 1, PV waves accumulate tile t - 2.  Tile t lives in
 // buffer t % 4.
-template <int kHG>
+template <int kHG, bool kWide>
 __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeParams p) {
   __shared__ Smem sm;
   constexpr int kHeadsWG = kHeads / kHG;
@@ -693,13 +702,13 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
     share_addr(wa, kTokP * pw, lane);
     if (ntiles > 0) {
 #pragma unroll
-      for (int u = 0; u < kDepth; ++u) load_share(regs[u], sm, p.kv, u * kTileTokens + kTokP * pw, n_valid, lane);
+      for (int u = 0; u < kDepth; ++u) load_share<kTokP, kWide>(regs[u], sm, p.kv, u * kTileTokens + kTokP * pw, n_valid, lane);
     }
     if (q_thread) stage_q(sm, qc, q_hl, q_chunk, p.scale_log2 < 0.f, lane);
     __syncthreads();   // q staged
     if (ntiles == 0) return;
     store_share(sm, regs[0], wa, 0, kTokP * pw, pw, lane);
-    load_share(regs[0], sm, p.kv, kDepth * kTileTokens + kTokP * pw, n_valid, lane);
+    load_share<kTokP, kWide>(regs[0], sm, p.kv, kDepth * kTileTokens + kTokP * pw, n_valid, lane);
     __syncthreads();   // B_0
     for (int t0 = 0; t0 + 1 < nstages; t0 += kDepth) {
 #pragma unroll
@@ -709,7 +718,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
         if (t + 1 < ntiles) store_share(sm, regs[nxt], wa, (t + 1) % kBufs, kTokP * pw, pw, lane);
         // issued on every path so the loads behind each ring slot are the
         // same wherever it is consumed (past the end they re-read a cached record)
-        load_share(regs[nxt], sm, p.kv, (t + 1 + kDepth) * kTileTokens + kTokP * pw, n_valid, lane);
+        load_share<kTokP, kWide>(regs[nxt], sm, p.kv, (t + 1 + kDepth) * kTileTokens + kTokP * pw, n_valid, lane);
         if (t + 1 < nstages) __syncthreads();   // B_{t+1}
       }
     }
@@ -957,7 +966,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_gather_kernel(const GatherPar
       Share<8> r;
       ShareAddr<8> wa;
       share_addr(wa, 8 * (wid - 4), lane);
-      load_share(r, sm, p.kv, t * kTileTokens + 8 * (wid - 4), n_valid, lane);
+      load_share<8, true>(r, sm, p.kv, t * kTileTokens + 8 * (wid - 4), n_valid, lane);
       store_share(sm, r, wa, 0, 8 * (wid - 4), wid - 4, lane);
     }
     __syncthreads();
@@ -993,10 +1002,19 @@ __global__ __launch_bounds__(kThreads, 1) void mla_gather_kernel(const GatherPar
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const int nblk = p.batch * p.nsplit * p.head_groups;
-  if (p.head_groups == 2)
-    hipLaunchKernelGGL(mla_decode_kernel<2>, dim3(nblk), dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL(mla_decode_kernel<1>, dim3(nblk), dim3(kThreads), 0, stream, p);
+  // gathers take 32-bit offsets when every byte of the pool lies within 4 GiB of its start
+  const bool wide = (uint64_t)p.num_pages * (uint64_t)p.page_stride > (1ull << 32);
+  if (p.head_groups == 2) {
+    if (wide)
+      hipLaunchKernelGGL((mla_decode_kernel<2, true>), dim3(nblk), dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((mla_decode_kernel<2, false>), dim3(nblk), dim3(kThreads), 0, stream, p);
+  } else {
+    if (wide)
+      hipLaunchKernelGGL((mla_decode_kernel<1, true>), dim3(nblk), dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((mla_decode_kernel<1, false>), dim3(nblk), dim3(kThreads), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

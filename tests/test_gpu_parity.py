@@ -573,6 +573,33 @@ def test_strided_views_match_contiguous():
     assert bool((lsebig[:, :3] == 3.0).all()) and bool((lsebig[:, 67:] == 3.0).all())
 
 
+def test_pool_reaching_past_4gib():
+    """A pool view whose pages lie 1 GiB + 16 bytes apart, so pages 4-6 start
+    beyond 2^32 bytes: the gathers take 64-bit offsets there (a pool within
+    4 GiB of its start takes 32-bit ones), and the results equal the compact
+    pool's bit for bit under both head groupings."""
+    w = _custom(4600, [600, 500], 512)
+    ref_out, ref_lse = O.sparse_mla_decode(w.q_bits, w.kv_pages, w.page_table, w.topk_idx, w.seq_lens,
+                                           w.softmax_scale)
+    stride = (1 << 30) + 16
+    P = w.num_pages
+    used = {int(x) for x in w.page_table.ravel() if x >= 0}
+    assert max(used) * stride >= 1 << 32, "a selected page must start past 4 GiB"
+    d = to_device(w)
+    big = torch.empty(P * stride, dtype=torch.uint8, device="cuda")
+    view = big.as_strided((P, 149504), (stride, 1))
+    view.copy_(d["kv_pages"])
+    v = dict(d, kv_pages=view)
+    print(f"pool view: {P} pages at stride {stride} ({P * stride / 2**30:.1f} GiB)", flush=True)
+    for hg in (1, 2):
+        o_ref, l_ref = decode(d, w.softmax_scale, head_groups=hg)
+        o, l = decode(v, w.softmax_scale, head_groups=hg)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(l, l_ref), f"head_groups={hg}"
+        check_attention(o, l, ref_out, ref_lse, label=f"pool past 4 GiB, {64 // hg}-head groups")
+    del big, view, v
+
+
 def test_split_merge_alternating_inputs():
     """The LSE combine reads partials the decode launch just wrote to the
     stream's scratch: alternate two input sets of one shape on one stream,
