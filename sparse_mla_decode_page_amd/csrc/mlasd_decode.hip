@@ -17,18 +17,20 @@
 //       only its own token) and dequantise them into an LDS tile buffer;
 //   QK waves (one per 32 heads, Q^T held in registers) compute S^T[32
 //       tokens][32 heads] = K Q^T of tile t on v_mfma_f32_32x32x16 (fp16 over
-//       the 448 nope dims, bf16 over the 64 rope dims) and, between those
-//       MFMAs, the online softmax of tile t - 1 in fp32 (exp2 domain),
-//       handing the fp16 P^T operand and the accumulator rescale factor to
-//       their PV waves through LDS.  In the 32-head kernel a second wave
+//       the 448 nope dims, bf16 over the 64 rope dims);
+//   the online softmax (fp32, exp2 domain) of a tile turns its scores into
+//       the fp16 P^T operand: in the 64-head kernel on the PV waves, one
+//       stage after the scores; in the 32-head kernel on the QK wave,
+//       between the next tile's MFMAs, handing P^T and the accumulator
+//       rescale factor to the PV waves through LDS.  There a second wave
 //       takes nope dims [192, 448) of the scores and hands its fp32 part
 //       over through LDS; the QK wave adds it one stage later;
 //   PV waves (two per QK wave, 224 output dims each) accumulate
-//       O^T[dims][heads] += V^T P^T of tile t - 2 on v_mfma_f32_32x32x16_f16,
-//       the V^T operand read from the token-major tile by
-//       ds_read_b64_tr_b16; they own O and write out (or fp32 partials).
-// Four tile buffers hold tiles t + 1, t, t - 1 (waiting for its P) and
-// t - 2.  One token-major fp16 tile serves both contractions (the nope dims
+//       O^T[dims][heads] += V^T P^T on v_mfma_f32_32x32x16_f16, the V^T
+//       operand read from the token-major tile by ds_read_b64_tr_b16; they
+//       own O and write out (or fp32 partials).
+// Four tile buffers hold the tiles in flight (the 32-head kernel's PV waves
+// run two tiles behind the scores, the 64-head kernel's one).  One token-major fp16 tile serves both contractions (the nope dims
 // are the K operand and V).  Before the loop every thread resolves and
 // compacts one index entry (a1) and converts a slice of Q to fp16.
 //
@@ -85,10 +87,6 @@ constexpr int kQkSplit = 12;              // 32-head kernel: nope k-steps of the
 
 struct __align__(16) Smem {
   uint16_t kv[kBufs][kTileTokens * kRowH];   // 4 x 32 KiB tile buffers
-  u32x4 pex[2][2][2][64];                 // [tile & 1][QK wave][k-step][lane]: P^T operand (fp16 x 8)
-  float aex[2][2][64];                    // [tile & 1][QK wave][lane]: O rescale factor
-  float lx[2][64];                        // [QK wave][lane]: final softmax sum
-  int32_t rx[2];                          // [QK wave]: final rebase reference R
   alignas(16) int32_t tflag[kBufs][4];    // [buffer][producer]: mask of rebased tokens
   alignas(16) int32_t rmax[kBufs][4];     // [buffer][producer]: largest rebase exponent
   alignas(16) int8_t rt[kBufs][kTileTokens];   // [buffer][row]: rebase exponent r_t of each row
@@ -97,7 +95,19 @@ struct __align__(16) Smem {
   uint16_t tok_entry[kMaxTopk];           //                 entry index in the slice
   int32_t wave_cnt[kWaves];
   alignas(16) float sf[4][16][8];        // [producer][token][group]: 2^(k_g - r_t) of the share's tokens
-  f32x4 sx[2][4][64];                     // [tile & 1][register quad][lane]: 32-head kernel, wave 7's partial scores
+  union {
+    // 64-head kernel: each QK wave hands a tile's raw scores S^T (fp32, in the
+    // QK MFMAs' layout) to its PV waves: [tile & 1][QK wave][register quad][lane]
+    f32x4 sx[2][2][4][64];
+    // 32-head kernel: the QK wave runs the softmax and hands P to its PV waves
+    struct {
+      u32x4 pex[2][2][64];   // [tile & 1][k-step][lane]: P^T operand (fp16 x 8)
+      float aex[2][64];      // [tile & 1][lane]: O rescale factor
+      float lx[64];          // [lane]: final softmax sum
+      int32_t rx;            // final rebase reference R
+      alignas(16) f32x4 sx2[2][4][64];   // [tile & 1][register quad][lane]: wave 7's part of the scores
+    } e;
+  } h;
 };
 static_assert(kHeads * kQRowH * 2 <= 3 * kTileTokens * kRowB, "q staging must fit tile buffers 1-3");
 static_assert(4 * 32 * kStageRowB <= 2 * kTileTokens * kRowB, "epilogue staging must fit two tile buffers");
@@ -633,15 +643,19 @@ __device__ __forceinline__ void store_pv(const DecodeParams& p, uint8_t* stage, 
 // kHG = 1: a workgroup computes all 64 heads of its (query, slice): QK
 // waves 0 and 1 (SIMDs 0, 1), producers 2 and 3 (16 tokens each, SIMDs 2,
 // 3), PV waves 4, 6 (heads 0-31, dims 0-223 / 224-447) and 5, 7 (heads
-// 32-63): each SIMD runs one MFMA-heavy wave and one lighter one.
+// 32-63): each SIMD runs one MFMA-heavy wave and one lighter one.  Stage t
+// (between barriers B_t and B_t+1, t = 0..ntiles): producers dequantise
+// tile t + 1, QK waves compute the scores of tile t and hand them over raw,
+// PV waves run the online softmax of tile t - 1 and accumulate it (each of
+// a QK wave's two PV waves computes the same P for its 32 heads).
 // kHG = 2: 32 heads: QK wave 0 (nope dims [0, 192) and rope), second QK
 // wave 7 (nope dims [192, 448)), PV waves 2 and 3, producers 1, 4, 5, 6 (8
-// tokens each).
-//
-// Stage t (between barriers B_t and B_t+1, t = 0..ntiles): producers
-// dequantise tile t + 1, QK waves compute the scores of tile t and the
-// softmax of tile t - 1, PV waves accumulate tile t - 2.  Tile t lives in
-// buffer t % 4.
+// tokens each).  Stage t (t = 0..ntiles + 1): producers dequantise tile
+// t + 1, the QK wave computes the scores of tile t and the softmax of tile
+// t - 1 between its MFMAs, PV waves accumulate tile t - 2.  (With the
+// softmax on the PV waves as in the 64-head kernel, the last tile's serial
+// softmax and P V cost more on short slices than the stage it saves.)
+// Tile t lives in buffer t % 4.
 template <int kHG, bool kWide>
 __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodeParams p) {
   __shared__ Smem sm;
@@ -688,7 +702,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
   const int n_valid =
       compact_slice(sm, idx, seq_len, pt_row, p.max_pages, p.num_pages, p.page_stride, pt_lds, n_staged);
   const int ntiles = (n_valid + kTileTokens - 1) / kTileTokens;
-  const int nstages = ntiles > 0 ? ntiles + 2 : 0;   // barriers B_0 .. B_ntiles+1
+  // barriers B_0 .. B_nstages-1: the 64-head kernel's PV waves run one stage
+  // behind the scores, the 32-head kernel's two (the softmax in between)
+  constexpr int kLag = kHG == 1 ? 1 : 2;
+  const int nstages = ntiles > 0 ? ntiles + kLag : 0;
 
   // 0 QK, 1 PV, 2 producer, 3 second QK wave (32-head kernel)
   const int role = kHG == 1 ? (wid < 2 ? 0 : (wid == 2 || wid == 3) ? 2 : 1)
@@ -770,7 +787,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
                                                              sm.rt[buf], half, acc, 0.f, m_unused, l_unused,
                                                              a_unused, nullptr);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) sm.sx[t & 1][c][lane] = f32x4{acc[4 * c], acc[4 * c + 1], acc[4 * c + 2], acc[4 * c + 3]};
+        for (int c = 0; c < 4; ++c)
+          sm.h.e.sx2[t & 1][c][lane] = f32x4{acc[4 * c], acc[4 * c + 1], acc[4 * c + 2], acc[4 * c + 3]};
       }
       __syncthreads();   // B_{t+1}
     }
@@ -778,158 +796,290 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
   }
 
   if (role == 1) {
-    // ---- PV waves: a6, two stages behind the scores ----
-    const int qk = kHG == 1 ? (wid & 1) : 0;   // the QK wave served (its 32 heads)
-    const int dhalf = kHG == 1 ? ((wid >> 1) & 1) : (wid & 1);
-    const int dim0 = 224 * dhalf;
-    f32x16 o[7];
+    if constexpr (kHG == 1) {
+      // ---- PV waves: a5 (online softmax) and a6 (P V), one stage behind the scores ----
+      const int qk = kHG == 1 ? (wid & 1) : 0;   // the QK wave served (its 32 heads)
+      const int dhalf = kHG == 1 ? ((wid >> 1) & 1) : (wid & 1);
+      const int dim0 = 224 * dhalf;
+      const int col = lane & 31, half = lane >> 5;
+      const int hl = 32 * qk + col;   // head within the workgroup
+      const float c_h = __builtin_ldexpf(fabsf(p.scale_log2), sm.eh[hl]);   // |scale| * log2(e) * 2^e_h
+      f32x16 o[7];
 #pragma unroll
-    for (int i = 0; i < 7; ++i) o[i] = f32x16{};
-    const int G = lane >> 4, c = lane & 15;
-    int voff[14];
+      for (int i = 0; i < 7; ++i) o[i] = f32x16{};
+      const int G = lane >> 4, c = lane & 15;
+      int voff[14];
 #pragma unroll
-    for (int m = 0; m < 7; ++m)
+      for (int m = 0; m < 7; ++m)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int r = 4 * (G >> 1) + (c >> 2) + 8 * h;
-        const int d = dim0 + 16 * (G & 1) + 4 * (c & 3) + 32 * m;
-        voff[2 * m + h] = r * kRowH + kChunkH * chunk_at(r, d >> 3) + (d & 7);
+        for (int h = 0; h < 2; ++h) {
+          const int r = 4 * (G >> 1) + (c >> 2) + 8 * h;
+          const int d = dim0 + 16 * (G & 1) + 4 * (c & 3) + 32 * m;
+          voff[2 * m + h] = r * kRowH + kChunkH * chunk_at(r, d >> 3) + (d & 7);
+        }
+      float m_run = -INFINITY, l_run = 0.f;
+      int R = kNoRebase;
+      __syncthreads();   // B_0
+      for (int t = 1; t < nstages; ++t) {
+        __syncthreads();   // B_t: the scores of tile t - 1 are in LDS
+        const int pt = t - 1, pbuf = pt % kBufs;
+        // S^T of tile pt, laid out as the QK MFMAs left it (lane l: head l % 32,
+        // rows 8 (i / 4) + 4 (l / 32) + i % 4); the 32-head kernel adds wave 7's part
+        f32x16 sc;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 x = sm.h.sx[pt & 1][qk][q4][lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sc[4 * q4 + e] = x[e];
+        }
+        float cs = c_h;
+        if (pt == ntiles - 1) {   // the last tile, possibly partial: scaled here, rows past the end -inf
+          const int tile_valid = n_valid - pt * kTileTokens;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int row = 8 * (i >> 2) + 4 * half + (i & 3);
+            sc[i] = row < tile_valid ? sc[i] * c_h : -INFINITY;
+          }
+          cs = 1.f;
+        }
+        float alpha = 1.f;
+        u32x4 pk[2];
+        Softmax st{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k <= 18; ++k) softmax_piece(k, st, sc, cs, m_run, l_run, alpha, pk);
+        // P V takes 2^(r_t - R) into P, R the running largest r_t (O rescaled
+        // by 2^(R_old - R_new) when it grows).
+        const i32x4 pf = *(const i32x4*)sm.tflag[pbuf];
+        const i32x4 pr = *(const i32x4*)sm.rmax[pbuf];
+        const uint32_t pflag = __builtin_amdgcn_readfirstlane(kProd == 2 ? pf.x | pf.y : pf.x | pf.y | pf.z | pf.w);
+        const int prt = __builtin_amdgcn_readfirstlane(
+            max(0, kProd == 2 ? max(pr.x, pr.y) : max(max(pr.x, pr.y), max(pr.z, pr.w))));
+        const int R_new = max(R, prt);
+        if (R_new != R) {
+          alpha = R == kNoRebase ? alpha : __builtin_ldexpf(alpha, R - R_new);
+          R = R_new;
+        }
+        if (pflag != 0 || R != 0) {   // rare: P takes 2^(r_t - R) per row (r_t - R <= 0)
+          const u32x4 pr0 = *(const u32x4*)&sm.rt[pbuf][0];
+          const u32x4 pr1 = *(const u32x4*)&sm.rt[pbuf][16];
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              f16x8& v = reinterpret_cast<f16x8*>(pk)[j];
+              v[i] = (_Float16)__builtin_ldexpf((float)v[i], row_rebase(pr0, pr1, 8 * j + i, half) - R);
+            }
+        }
+        if (__ballot(alpha != 1.f) != 0) {
+#pragma unroll
+          for (int i = 0; i < 7; ++i) o[i] *= alpha;
+        }
+        const f16x8 pb[2] = {__builtin_bit_cast(f16x8, pk[0]), __builtin_bit_cast(f16x8, pk[1])};
+        pv_tile<7>(o, sm.kv[pbuf], voff, pb);
       }
-    __syncthreads();   // B_0
-    __syncthreads();   // B_1
-    for (int t = 2; t < nstages; ++t) {
-      __syncthreads();   // B_t: P of tile t - 2 is in LDS
-      const int pt = t - 2;
-      f16x8 pb[2];
-      pb[0] = __builtin_bit_cast(f16x8, sm.pex[pt & 1][qk][0][lane]);
-      pb[1] = __builtin_bit_cast(f16x8, sm.pex[pt & 1][qk][1][lane]);
-      const float a = sm.aex[pt & 1][qk][lane];
-      if (__ballot(a != 1.f) != 0) {
-#pragma unroll
-        for (int i = 0; i < 7; ++i) o[i] *= a;
+      const float l = pair_sum(l_run);
+      const float mul = l > 0.f ? __builtin_ldexpf(1.f / l, R == kNoRebase ? 0 : R) : 0.f;
+      // staging: two slots in each of the tile buffers the last P V does not read
+      const int slot = kHG == 1 ? wid - 4 : dhalf;
+      const int sbuf = (ntiles + (slot >> 1)) % kBufs;
+      uint8_t* stage = (uint8_t*)&sm.kv[sbuf][0] + (slot & 1) * (32 * kStageRowB);
+      store_pv(p, stage, o, mul, b, s, head_base + 32 * qk, dim0, lane);
+      // a7 (lse): lanes 0..31 of the wave with the first 224 dims write their head
+      if (dhalf == 0 && half == 0) {
+        const float lse_v = l > 0.f ? (m_run + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -INFINITY;
+        const int head = head_base + hl;
+        if (p.nsplit == 1)
+          p.lse[(int64_t)b * p.lse_sb + head] = lse_v;
+        else
+          p.part_lse[((int64_t)b * p.nsplit + s) * kHeads + head] = lse_v;
       }
-      pv_tile<7>(o, sm.kv[pt % kBufs], voff, pb);
+
+    } else {
+      // ---- PV waves: a6, two stages behind the scores ----
+      const int qk = kHG == 1 ? (wid & 1) : 0;   // the QK wave served (its 32 heads)
+      const int dhalf = kHG == 1 ? ((wid >> 1) & 1) : (wid & 1);
+      const int dim0 = 224 * dhalf;
+      f32x16 o[7];
+#pragma unroll
+      for (int i = 0; i < 7; ++i) o[i] = f32x16{};
+      const int G = lane >> 4, c = lane & 15;
+      int voff[14];
+#pragma unroll
+      for (int m = 0; m < 7; ++m)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int r = 4 * (G >> 1) + (c >> 2) + 8 * h;
+          const int d = dim0 + 16 * (G & 1) + 4 * (c & 3) + 32 * m;
+          voff[2 * m + h] = r * kRowH + kChunkH * chunk_at(r, d >> 3) + (d & 7);
+        }
+      __syncthreads();   // B_0
+      __syncthreads();   // B_1
+      for (int t = 2; t < nstages; ++t) {
+        __syncthreads();   // B_t: P of tile t - 2 is in LDS
+        const int pt = t - 2;
+        f16x8 pb[2];
+        pb[0] = __builtin_bit_cast(f16x8, sm.h.e.pex[pt & 1][0][lane]);
+        pb[1] = __builtin_bit_cast(f16x8, sm.h.e.pex[pt & 1][1][lane]);
+        const float a = sm.h.e.aex[pt & 1][lane];
+        if (__ballot(a != 1.f) != 0) {
+#pragma unroll
+          for (int i = 0; i < 7; ++i) o[i] *= a;
+        }
+        pv_tile<7>(o, sm.kv[pt % kBufs], voff, pb);
+      }
+      // the QK wave wrote the final l and R before the last barrier
+      const float l = sm.h.e.lx[lane];
+      const int R = sm.h.e.rx;
+      const float mul = l > 0.f ? __builtin_ldexpf(1.f / l, R == kNoRebase ? 0 : R) : 0.f;
+      // staging: two slots in each of the tile buffers the last P V does not read
+      const int slot = kHG == 1 ? wid - 4 : dhalf;
+      const int sbuf = (ntiles + (slot >> 1)) % kBufs;
+      uint8_t* stage = (uint8_t*)&sm.kv[sbuf][0] + (slot & 1) * (32 * kStageRowB);
+      store_pv(p, stage, o, mul, b, s, head_base + 32 * qk, dim0, lane);
+
     }
-    // the QK wave wrote the final l and R before the last barrier
-    const float l = sm.lx[qk][lane];
-    const int R = sm.rx[qk];
-    const float mul = l > 0.f ? __builtin_ldexpf(1.f / l, R == kNoRebase ? 0 : R) : 0.f;
-    // staging: two slots in each of the tile buffers the last P V does not read
-    const int slot = kHG == 1 ? wid - 4 : dhalf;
-    const int sbuf = (ntiles + (slot >> 1)) % kBufs;
-    uint8_t* stage = (uint8_t*)&sm.kv[sbuf][0] + (slot & 1) * (32 * kStageRowB);
-    store_pv(p, stage, o, mul, b, s, head_base + 32 * qk, dim0, lane);
     return;
   }
 
-  // ---- QK waves: a4 (scores) and a5 (online softmax) ----
-  const int qk = kHG == 1 ? wid : 0;
-  const int col = lane & 31, half = lane >> 5;
-  const int hl = 32 * qk + col;                      // head within the workgroup
-  constexpr int kQkN = kHG == 2 ? kQkSplit : kNopeSteps;   // nope k-steps of this wave
-  QRegs<0, kQkN, true> q;
-  {
-    const uint16_t* qs = reinterpret_cast<const uint16_t*>(&sm.kv[1][0]) + hl * kQRowH + 8 * half;
+  if constexpr (kHG == 1) {
+    // ---- QK waves: a4 (scores), handed to the PV waves through LDS ----
+    const int qk = wid;
+    const int col = lane & 31, half = lane >> 5;
+    const int hl = 32 * qk + col;                      // head within the workgroup
+    constexpr int kQkN = kNopeSteps;                   // nope k-steps of this wave
+    QRegs<0, kQkN, true> q;
+    {
+      const uint16_t* qs = reinterpret_cast<const uint16_t*>(&sm.kv[1][0]) + hl * kQRowH + 8 * half;
 #pragma unroll
-    for (int k = 0; k < kQkN; ++k) q.n[k] = *(const f16x8*)(qs + 16 * k);
+      for (int k = 0; k < kQkN; ++k) q.n[k] = *(const f16x8*)(qs + 16 * k);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) q.r[k] = *(const bf16x8*)(qs + kDNope + 16 * k);
-  }
-  const float c_h = __builtin_ldexpf(fabsf(p.scale_log2), sm.eh[hl]);   // |scale| * log2(e) * 2^e_h
-  int koff[8];   // k-step k % 8 -> the lane's chunk in its row's 16-chunk block k / 8
+      for (int k = 0; k < 4; ++k) q.r[k] = *(const bf16x8*)(qs + kDNope + 16 * k);
+    }
+    int koff[8];   // k-step k % 8 -> the lane's chunk in its row's 16-chunk block k / 8
 #pragma unroll
-  for (int j = 0; j < 8; ++j) koff[j] = kChunkH * chunk_at(col, 2 * j + half);
-  float m_run = -INFINITY, l_run = 0.f;
-  int R = kNoRebase;
-  __syncthreads();   // B_0
+    for (int j = 0; j < 8; ++j) koff[j] = kChunkH * chunk_at(col, 2 * j + half);
+    __syncthreads();   // B_0
+    f32x16 acc;
+    float m_unused = 0.f, l_unused = 0.f, a_unused = 1.f;
+    for (int t = 0; t + 1 < nstages; ++t) {   // stage t: Q K^T of tile t
+      const int buf = t % kBufs;
+      qk_stage<false, kProd, 0, kQkN, true>(&sm.kv[buf][col * kRowH], koff, q, acc, sm.tflag[buf], sm.rt[buf], half,
+                                            acc, 0.f, m_unused, l_unused, a_unused, nullptr);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        sm.h.sx[t & 1][qk][c][lane] = f32x4{acc[4 * c], acc[4 * c + 1], acc[4 * c + 2], acc[4 * c + 3]};
+      __syncthreads();   // B_{t+1}
+    }
+  } else {
+    // ---- QK wave: a4 (scores) and a5 (online softmax) ----
+    const int qk = 0;
+    const int col = lane & 31, half = lane >> 5;
+    const int hl = col;                                // head within the workgroup
+    constexpr int kQkN = kQkSplit;                     // nope k-steps of this wave; wave 7 has the rest
+    QRegs<0, kQkN, true> q;
+    {
+      const uint16_t* qs = reinterpret_cast<const uint16_t*>(&sm.kv[1][0]) + hl * kQRowH + 8 * half;
+#pragma unroll
+      for (int k = 0; k < kQkN; ++k) q.n[k] = *(const f16x8*)(qs + 16 * k);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) q.r[k] = *(const bf16x8*)(qs + kDNope + 16 * k);
+    }
+    const float c_h = __builtin_ldexpf(fabsf(p.scale_log2), sm.eh[hl]);   // |scale| * log2(e) * 2^e_h
+    int koff[8];   // k-step k % 8 -> the lane's chunk in its row's 16-chunk block k / 8
+#pragma unroll
+    for (int j = 0; j < 8; ++j) koff[j] = kChunkH * chunk_at(col, 2 * j + half);
+    float m_run = -INFINITY, l_run = 0.f;
+    int R = kNoRebase;
+    __syncthreads();   // B_0
 
-  // stage t: Q K^T of tile t (t < ntiles) into `cur`, softmax of tile t - 1
-  // from `prev` (the two accumulators alternate, so the next stage's MFMAs
-  // never wait for this one's softmax to have read its scores)
-  auto stage = [&](int t, f32x16& cur, f32x16& prev) {
-    const int buf = t % kBufs, pbuf = (t + kBufs - 1) % kBufs;
-    const uint16_t* krow = &sm.kv[buf][col * kRowH];
-    const i32x4 pf = *(const i32x4*)sm.tflag[pbuf];   // the previous tile's flags, used after the MFMAs
-    const i32x4 pr = *(const i32x4*)sm.rmax[pbuf];
-    float alpha = 1.f;
-    u32x4 pk[2];
-    if constexpr (kHG == 2) {
-      if (t > 0) {   // wave 7's part of the previous tile's scores
+    // stage t: Q K^T of tile t (t < ntiles) into `cur`, softmax of tile t - 1
+    // from `prev` (the two accumulators alternate, so the next stage's MFMAs
+    // never wait for this one's softmax to have read its scores)
+    auto stage = [&](int t, f32x16& cur, f32x16& prev) {
+      const int buf = t % kBufs, pbuf = (t + kBufs - 1) % kBufs;
+      const uint16_t* krow = &sm.kv[buf][col * kRowH];
+      const i32x4 pf = *(const i32x4*)sm.tflag[pbuf];   // the previous tile's flags, used after the MFMAs
+      const i32x4 pr = *(const i32x4*)sm.rmax[pbuf];
+      float alpha = 1.f;
+      u32x4 pk[2];
+      if constexpr (kHG == 2) {
+        if (t > 0) {   // wave 7's part of the previous tile's scores
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const f32x4 x = sm.sx[(t - 1) & 1][c][lane];
+          for (int c = 0; c < 4; ++c) {
+            const f32x4 x = sm.h.e.sx2[(t - 1) & 1][c][lane];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) prev[4 * c + e] += x[e];
+            for (int e = 0; e < 4; ++e) prev[4 * c + e] += x[e];
+          }
         }
       }
+      if (t == 0) {
+        qk_stage<false, kProd, 0, kQkN, true>(krow, koff, q, cur, sm.tflag[buf], sm.rt[buf], half, prev, c_h, m_run,
+                                              l_run, alpha, pk);
+      } else if (t < ntiles) {
+        qk_stage<true, kProd, 0, kQkN, true>(krow, koff, q, cur, sm.tflag[buf], sm.rt[buf], half, prev, c_h, m_run,
+                                             l_run, alpha, pk);
+      } else {
+        // the last tile, possibly partial: scaled here, rows past the end -inf
+        const int tile_valid = n_valid - (t - 1) * kTileTokens;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = 8 * (i >> 2) + 4 * half + (i & 3);
+          prev[i] = row < tile_valid ? prev[i] * c_h : -INFINITY;
+        }
+        Softmax st{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k <= 18; ++k) softmax_piece(k, st, prev, 1.f, m_run, l_run, alpha, pk);
+      }
+      if (t > 0) {
+        const uint32_t pflag =
+            __builtin_amdgcn_readfirstlane(kProd == 2 ? pf.x | pf.y : pf.x | pf.y | pf.z | pf.w);
+        const int prt = __builtin_amdgcn_readfirstlane(
+            max(0, kProd == 2 ? max(pr.x, pr.y) : max(max(pr.x, pr.y), max(pr.z, pr.w))));
+        // P V takes 2^(r_t - R) into P, R the running largest r_t (O rescaled
+        // by 2^(R_old - R_new) when it grows).
+        const int R_new = max(R, prt);
+        if (R_new != R) {
+          alpha = R == kNoRebase ? alpha : __builtin_ldexpf(alpha, R - R_new);
+          R = R_new;
+        }
+        if (pflag != 0 || R != 0) {   // rare: P takes 2^(r_t - R) per row (r_t - R <= 0)
+          const u32x4 pr0 = *(const u32x4*)&sm.rt[pbuf][0];
+          const u32x4 pr1 = *(const u32x4*)&sm.rt[pbuf][16];
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              f16x8& v = reinterpret_cast<f16x8*>(pk)[j];
+              v[i] = (_Float16)__builtin_ldexpf((float)v[i], row_rebase(pr0, pr1, 8 * j + i, half) - R);
+            }
+        }
+        const int pt = t - 1;
+        sm.h.e.pex[pt & 1][0][lane] = pk[0];
+        sm.h.e.pex[pt & 1][1][lane] = pk[1];
+        sm.h.e.aex[pt & 1][lane] = alpha;
+        if (t == ntiles) {   // the PV waves' epilogue reads the final l and R
+          sm.h.e.lx[lane] = pair_sum(l_run);
+          if (lane == 0) sm.h.e.rx = R;
+        }
+      }
+      __syncthreads();   // B_{t+1}
+    };
+    f32x16 acc0, acc1;
+    acc1 = f32x16{};
+    for (int t = 0; t + 1 < nstages; t += 2) {
+      stage(t, acc0, acc1);
+      if (t + 2 < nstages) stage(t + 1, acc1, acc0);
     }
-    if (t == 0) {
-      qk_stage<false, kProd, 0, kQkN, true>(krow, koff, q, cur, sm.tflag[buf], sm.rt[buf], half, prev, c_h, m_run,
-                                            l_run, alpha, pk);
-    } else if (t < ntiles) {
-      qk_stage<true, kProd, 0, kQkN, true>(krow, koff, q, cur, sm.tflag[buf], sm.rt[buf], half, prev, c_h, m_run,
-                                           l_run, alpha, pk);
-    } else {
-      // the last tile, possibly partial: scaled here, rows past the end -inf
-      const int tile_valid = n_valid - (t - 1) * kTileTokens;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = 8 * (i >> 2) + 4 * half + (i & 3);
-        prev[i] = row < tile_valid ? prev[i] * c_h : -INFINITY;
-      }
-      Softmax st{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k = 0; k <= 18; ++k) softmax_piece(k, st, prev, 1.f, m_run, l_run, alpha, pk);
+    // a7 (lse): lanes 0..31 write their head
+    const float l = pair_sum(l_run);
+    const float lse_v = l > 0.f ? (m_run + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -INFINITY;
+    if (half == 0) {
+      const int head = head_base + hl;
+      if (p.nsplit == 1)
+        p.lse[(int64_t)b * p.lse_sb + head] = lse_v;
+      else
+        p.part_lse[((int64_t)b * p.nsplit + s) * kHeads + head] = lse_v;
     }
-    if (t > 0) {
-      const uint32_t pflag =
-          __builtin_amdgcn_readfirstlane(kProd == 2 ? pf.x | pf.y : pf.x | pf.y | pf.z | pf.w);
-      const int prt = __builtin_amdgcn_readfirstlane(
-          max(0, kProd == 2 ? max(pr.x, pr.y) : max(max(pr.x, pr.y), max(pr.z, pr.w))));
-      // P V takes 2^(r_t - R) into P, R the running largest r_t (O rescaled
-      // by 2^(R_old - R_new) when it grows).
-      const int R_new = max(R, prt);
-      if (R_new != R) {
-        alpha = R == kNoRebase ? alpha : __builtin_ldexpf(alpha, R - R_new);
-        R = R_new;
-      }
-      if (pflag != 0 || R != 0) {   // rare: P takes 2^(r_t - R) per row (r_t - R <= 0)
-        const u32x4 pr0 = *(const u32x4*)&sm.rt[pbuf][0];
-        const u32x4 pr1 = *(const u32x4*)&sm.rt[pbuf][16];
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            f16x8& v = reinterpret_cast<f16x8*>(pk)[j];
-            v[i] = (_Float16)__builtin_ldexpf((float)v[i], row_rebase(pr0, pr1, 8 * j + i, half) - R);
-          }
-      }
-      const int pt = t - 1;
-      sm.pex[pt & 1][qk][0][lane] = pk[0];
-      sm.pex[pt & 1][qk][1][lane] = pk[1];
-      sm.aex[pt & 1][qk][lane] = alpha;
-      if (t == ntiles) {   // the PV waves' epilogue reads the final l and R
-        sm.lx[qk][lane] = pair_sum(l_run);
-        if (lane == 0) sm.rx[qk] = R;
-      }
-    }
-    __syncthreads();   // B_{t+1}
-  };
-  f32x16 acc0, acc1;
-  acc1 = f32x16{};
-  for (int t = 0; t + 1 < nstages; t += 2) {
-    stage(t, acc0, acc1);
-    if (t + 2 < nstages) stage(t + 1, acc1, acc0);
-  }
-  // a7 (lse): lanes 0..31 write their head
-  const float l = pair_sum(l_run);
-  const float lse_v = l > 0.f ? (m_run + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -INFINITY;
-  if (half == 0) {
-    const int head = head_base + hl;
-    if (p.nsplit == 1)
-      p.lse[(int64_t)b * p.lse_sb + head] = lse_v;
-    else
-      p.part_lse[((int64_t)b * p.nsplit + s) * kHeads + head] = lse_v;
   }
 }
 
