@@ -77,7 +77,7 @@ constexpr int kNopeSteps = kDNope / 16;   // 28 fp16 k-steps of Q K^T; 4 bf16 ro
 constexpr int kQkAhead = 2;               // Q K^T operand k-steps read ahead
 constexpr int kPvAhead = 2;               // P V operand blocks read ahead
 constexpr int kDepth = 2;                 // tiles gathered ahead by the producers
-constexpr int kBufs = 4;                  // tile buffers: producers t + 1, Q K^T t, P V t - 2 (t - 1 held)
+constexpr int kBufs = 4;                  // tile buffers: producers t + 1, Q K^T t, P V t - 1 (64 heads) or t - 2
 constexpr int kPtStaged = kTileTokens * kRowB / 4;   // page-table entries staged in tile buffer 0
 constexpr float kRescaleLog2 = 8.f;       // lazy-rescale threshold: P <= 2^8
 constexpr int kQRowH = 520;               // Q staging row (16-bit units): 512 + 8 pad
@@ -797,7 +797,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
 
   if (role == 1) {
     if constexpr (kHG == 1) {
-      // ---- PV waves: a5 (online softmax) and a6 (P V), one stage behind the scores ----
+      // ---- PV waves (64 heads): a5 (online softmax) and a6 (P V), one stage behind the scores ----
       const int qk = kHG == 1 ? (wid & 1) : 0;   // the QK wave served (its 32 heads)
       const int dhalf = kHG == 1 ? ((wid >> 1) & 1) : (wid & 1);
       const int dim0 = 224 * dhalf;
@@ -895,7 +895,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const DecodePar
       }
 
     } else {
-      // ---- PV waves: a6, two stages behind the scores ----
+      // ---- PV waves (32 heads): a6, two stages behind the scores ----
       const int qk = kHG == 1 ? (wid & 1) : 0;   // the QK wave served (its 32 heads)
       const int dhalf = kHG == 1 ? ((wid >> 1) & 1) : (wid & 1);
       const int dim0 = 224 * dhalf;
