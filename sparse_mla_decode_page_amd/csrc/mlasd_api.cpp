@@ -219,8 +219,15 @@ int reserve_workspace(hipStream_t stream, size_t bytes) {
 // sibling reads the gathered records from L2), the rest in top-k slices of at
 // least kMinAutoSlice entries (each extra slice costs an fp32 partial write
 // and read, and below two tiles a workgroup's fixed start-up cost
-// dominates).  A slice holds a whole number of 32-token tiles.
+// dominates).  A slice holds a whole number of 32-token tiles.  The split is
+// then kept only if the tiles it takes off each workgroup pay for the
+// combine launch and the added workgroups: measured on 256 CUs, a tile costs
+// a workgroup about 0.95 us and a split about 2.5 us + 0.035 us per (query x
+// slice) (split against unsplit for B = 1..64 and top-k 128..512).
 constexpr int kMinAutoSlice = 64;
+constexpr int64_t kTileNs = 950;             // per tile of a workgroup's slice
+constexpr int64_t kSplitNs = 2500;           // a split: fixed part
+constexpr int64_t kSplitNsPerSlice = 35;     //          per (query x slice)
 
 void make_plan(int32_t batch, int32_t topk, int32_t ns_request, int32_t hg_request, int cus,
                int32_t* nsplit, int32_t* split_len, int32_t* head_groups) {
@@ -241,6 +248,13 @@ void make_plan(int32_t batch, int32_t topk, int32_t ns_request, int32_t hg_reque
   int len = topk > 0 ? (topk + ns - 1) / ns : tile;
   len = (len + tile - 1) / tile * tile;
   ns = topk > 0 ? (topk + len - 1) / len : 1;
+  if (ns_request <= 0 && ns > 1) {
+    const int64_t saved = max_split - len / tile;   // tiles taken off each workgroup
+    if (saved * kTileNs <= kSplitNs + kSplitNsPerSlice * (int64_t)batch * ns) {
+      ns = 1;
+      len = (topk + tile - 1) / tile * tile;
+    }
+  }
   *nsplit = ns;
   *split_len = len;
   *head_groups = hg;

@@ -280,7 +280,13 @@ def test_append_zero_tokens_is_a_noop():
     (64, 512, 1, 256, (1, 512, 2)),    # forced
     (64, 512, 3, 256, (3, 192, 2)),    # slices hold whole 32-token tiles
     (64, 512, 99, 256, (16, 32, 2)),   # clamped to ceil(topk/32)
-    (8, 100, 0, 80, (2, 64, 2)),       # 10 workgroups per query
+    (8, 100, 0, 80, (1, 128, 2)),      # 10 workgroups per query, but 2 slices of 2 tiles do not pay for a split
+    (64, 256, 0, 256, (1, 256, 2)),    # 2 slices would take 4 tiles off each workgroup: not worth a combine
+    (64, 128, 0, 256, (1, 128, 2)),
+    (1, 128, 0, 256, (1, 128, 2)),
+    (1, 256, 0, 256, (4, 64, 2)),      # 6 tiles off each workgroup: split
+    (16, 256, 0, 256, (4, 64, 2)),
+    (48, 512, 0, 256, (2, 256, 2)),
     (32, 512, 0, 80, (1, 512, 2)),
 ])
 def test_plan(batch, topk, req, cus, expect):
