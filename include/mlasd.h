@@ -116,8 +116,10 @@ typedef struct mlasd_tensor {
  *   stream     HIP stream to enqueue on.
  *
  * B == 0 is a no-op.  topk == 0 writes out = 0, lse = -inf.
- * When the plan cuts a query's top-k list into slices (small batches), the
- * fp32 partial results live in the split scratch reserved for `stream` by
+ * The automatic plan cuts a query's top-k list into slices only when the
+ * batch leaves compute units idle and the tiles it takes off each
+ * workgroup outweigh the cost of the LSE combine.  Then the fp32 partial
+ * results live in the split scratch reserved for `stream` by
  * mlasd_prepare (or mlasd_reserve); if that scratch is missing or too small
  * the call returns MLASD_ERR_WORKSPACE and enqueues nothing.  It never
  * allocates, frees or synchronises, so it may be captured into a graph.
@@ -149,8 +151,12 @@ int mla_sparse_decode(const mlasd_tensor* q, const mlasd_tensor* kv_pages,
  *                workgroups of 32 heads share the slice's gathered records.
  *                0: automatic for the chosen nsplit.  Other values:
  *                MLASD_ERR_SHAPE.
- * Results equal mla_sparse_decode's up to floating-point rounding (the head
- * groups do not change any value; the slices change the summation order).
+ * Results equal mla_sparse_decode's up to floating-point rounding: the
+ * slices change the summation order of the softmax-weighted sum, and with 2
+ * head groups each score is summed over the 512 dims in two parts (dims
+ * 0..191 with the rope dims, and 192..447) that are then added, where 1
+ * head group sums it in one pass.  The 64-head and 32-head results
+ * therefore differ in the last bits; neither is the more exact.
  * Split plans need scratch as mla_sparse_decode does; mla_sparse_workspace_size
  * gives the bytes for mlasd_reserve.  Intended for tests and benchmarks.
  */

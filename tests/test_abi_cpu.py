@@ -218,6 +218,20 @@ def test_workspace_size_host_only():
         m.workspace_size(1, 512, 0, 3, 256)
 
 
+@pytest.mark.parametrize("cus", [256, 304, 80])
+def test_prepare_bound_covers_smaller_topk(cus):
+    """mlasd_prepare sizes the scratch from the automatic plans at max_topk
+    for every batch up to max_batch.  That bound must hold for every smaller
+    top-k too, although the plan drops a split that does not pay for its
+    combine: check it over all top-k values for several max_batch."""
+    for max_batch in (1, 2, 3, 8, 16, 64, 128):
+        for max_topk in (64, 192, 256, 300, 512):
+            bound = max(m.workspace_size(b, max_topk, 0, 0, cus) for b in range(1, max_batch + 1))
+            for b in range(1, max_batch + 1):
+                for k in range(1, max_topk + 1, 3):
+                    assert m.workspace_size(b, k, 0, 0, cus) <= bound, (cus, max_batch, max_topk, b, k)
+
+
 def _append_args(n=4, B=2, max_pages=2, num_pages=3):
     return dict(lat=_t(0x10000, BF16, [n, 512]), seq=_t(0x20000, I32, [n]), pos=_t(0x30000, I32, [n]),
                 pt=_t(0x40000, I32, [B, max_pages]), kv=_t(0x50000, U8, [num_pages, 149504]))
