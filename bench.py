@@ -203,37 +203,47 @@ def bench_append(dev, kv, pt, seq_len, steps, stream):
             "workload": f"{B} sequences x {per_seq} new tokens into the resident pool"}
 
 
-def bench_topk(dev, stream, steps, batch=64, max_len=65536, k=512):
+def bench_topk(dev, stream, steps, batch=64, max_len=65536, k=512, parts=None):
     """Time mla_topk_select on `batch` rows of `max_len` fp32 scores (all
     positions candidates): HIP events on the launch stream around `steps`
-    calls captured in one graph."""
+    calls captured in one graph.  The stream's scratch is reserved for the
+    library's plan (or the forced `parts`); the one-workgroup-per-row plan
+    is timed beside it."""
     import torch
     import sparse_mla_decode_page_amd as mlasd
     from gen.synth import indexer_scores
     sc = torch.from_numpy(indexer_scores(31, batch, max_len)).to(dev)
     lens = torch.full((batch,), max_len, dtype=torch.int32, device=dev)
     idx = torch.empty((batch, k), dtype=torch.int32, device=dev)
-    with torch.cuda.stream(stream):
-        for _ in range(3):
-            mlasd.mla_topk_select(sc, lens, k, out=idx, stream=stream)
-    stream.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        for _ in range(steps):
-            mlasd.mla_topk_select(sc, lens, k, out=idx, stream=stream)
-    with torch.cuda.stream(stream):
-        g.replay()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        g.replay()
-        e1.record(stream)
-    stream.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / steps
+    n_parts, nbytes = mlasd.topk_plan(batch, max_len, parts or 0)
+    mlasd.reserve(nbytes, stream=stream)
+
+    def timed(pa):
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                mlasd.mla_topk_select(sc, lens, k, out=idx, stream=stream, parts=pa)
+        stream.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(steps):
+                mlasd.mla_topk_select(sc, lens, k, out=idx, stream=stream, parts=pa)
+        with torch.cuda.stream(stream):
+            g.replay()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        stream.synchronize()
+        del g
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+    us = timed(parts)
+    us_one = timed(1) if n_parts > 1 else us
     byts = batch * max_len * 4 + batch * k * 4 + batch * 4
     gbs = byts / (us * 1e-6) / 1e9
-    del g
     return {"workload": f"{batch} queries x {max_len} fp32 scores, k={k}", "us_per_launch": us,
+            "parts_per_row": n_parts, "us_per_launch_one_workgroup_per_row": us_one,
             "rows_per_s": batch / (us * 1e-6),
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": byts},
@@ -250,6 +260,8 @@ def bench_chain(dev, wb, steps):
     w = wb.w
     sc = torch.from_numpy(indexer_scores(33, w.batch, int(w.seq_lens.max()))).to(dev)
     idx = torch.empty((w.batch, w.topk), dtype=torch.int32, device=dev)
+    n_parts, nbytes = mlasd.topk_plan(w.batch, sc.shape[1])
+    mlasd.reserve(nbytes, stream=wb.stream)   # the decode's split scratch, grown if the selection needs more
     q = wb.dsets[0]["q"]
     out = torch.empty((w.batch, 64, 448), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.batch, 64), dtype=torch.float32, device=dev)
@@ -279,7 +291,8 @@ def bench_chain(dev, wb, steps):
     del g
     return {"workload": f"top-k of {w.batch} x {int(w.seq_lens.max())} fp32 scores (k={w.topk}), then the "
                         f"decode of workload c3 on the selected entries",
-            "us_per_step": us, "launch": f"HIP graph replay of {steps} chained steps"}
+            "us_per_step": us, "topk_parts_per_row": n_parts,
+            "launch": f"HIP graph replay of {steps} chained steps"}
 
 
 class Workbench:
@@ -468,7 +481,8 @@ def main():
     ap.add_argument("--batch", type=int, default=0, help="custom workload: queries")
     ap.add_argument("--topk", type=int, default=512, help="custom workload: top-k width")
     ap.add_argument("--seq-len", type=int, default=65536, help="custom workload: tokens per sequence")
-    ap.add_argument("--nsplit", type=int, default=0, help="force top-k slices per query (0 = plan)")
+    ap.add_argument("--nsplit", type=int, default=0,
+                    help="force top-k slices per query (0 = plan); with --op topk, parts per row")
     ap.add_argument("--head-groups", type=int, default=0, help="force workgroups per slice's heads (0 = plan)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -525,7 +539,7 @@ def main():
         return
     if args.op == "topk":
         res = bench_topk(dev, torch.cuda.Stream(dev), args.steps, batch=args.batch or 64,
-                         max_len=args.seq_len, k=args.topk)
+                         max_len=args.seq_len, k=args.topk, parts=args.nsplit or None)
         res["metric"] = "top-k selection: query rows/s"
         print(json.dumps(res), flush=True)
         return

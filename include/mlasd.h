@@ -270,10 +270,40 @@ int mla_kv_append(const mlasd_tensor* latent, const mlasd_tensor* seq_ids,
  *             as -inf, -0.0 equal to +0.0 -- then -1.
  *   stream    HIP stream to enqueue on.
  * B == 0 or k == 0 is a no-op.  Allocates nothing and never synchronises.
+ * Plan: when max_len is at least 65,536 and the batch leaves at least 4
+ * compute units per row (mla_topk_plan), the candidate pass over each long
+ * row is cut into 4 to 8 parts of one workgroup each, whose candidate lists
+ * go to the split scratch reserved for `stream` (mlasd_reserve with
+ * mla_topk_plan's bytes); a second launch selects and sorts each row.
+ * Without enough scratch the call runs one workgroup per row instead.  Both
+ * give the same result, bit for bit.
  * Returns MLASD_OK or a negative MLASD_ERR_* code.
  */
 int mla_topk_select(const mlasd_tensor* scores, const mlasd_tensor* seq_lens, const mlasd_tensor* topk_idx,
                     mlasd_stream_t stream);
+
+/*
+ * mla_topk_select_ex -- mla_topk_select with the parts per row forced:
+ * parts <= 0 as mla_topk_select; 1 one workgroup per row; 2..8 that many
+ * parts for rows longer than max(k, 4096) positions (shorter rows are
+ * selected whole), needing mla_topk_plan's bytes of the stream's split
+ * scratch (MLASD_ERR_WORKSPACE without them, nothing enqueued).  parts > 8:
+ * MLASD_ERR_SHAPE.  Same results as mla_topk_select.  Intended for tests
+ * and benchmarks.
+ */
+int mla_topk_select_ex(const mlasd_tensor* scores, const mlasd_tensor* seq_lens, const mlasd_tensor* topk_idx,
+                       int32_t parts, mlasd_stream_t stream);
+
+/*
+ * mla_topk_plan -- the parts per row mla_topk_select would use for B rows of
+ * max_len scores (host only; parts_request as in mla_topk_select_ex), and
+ * the bytes of split scratch that plan needs (0 for one part).  num_cus > 0
+ * plans for that many compute units; num_cus <= 0 queries the current HIP
+ * device (only when parts_request <= 0).  Errors: MLASD_ERR_NULL,
+ * MLASD_ERR_SHAPE (negative sizes, parts_request > 8), MLASD_ERR_DEVICE.
+ */
+int mla_topk_plan(int32_t batch, int32_t max_len, int32_t parts_request, int32_t num_cus, int32_t* parts,
+                  size_t* bytes);
 
 /*
  * mlasd_prepare -- reserve the split scratch of `stream` (on the current
@@ -291,7 +321,8 @@ int mla_topk_select(const mlasd_tensor* scores, const mlasd_tensor* seq_lens, co
 int mlasd_prepare(mlasd_stream_t stream, int32_t max_batch, int32_t max_topk);
 
 /* mlasd_reserve -- as mlasd_prepare, for at least `bytes` of split scratch
- * (e.g. mla_sparse_workspace_size of a forced plan). */
+ * (e.g. mla_sparse_workspace_size of a forced plan, or mla_topk_plan's
+ * bytes; the top-k selection and the decode share the stream's scratch). */
 int mlasd_reserve(mlasd_stream_t stream, size_t bytes);
 
 /*

@@ -19,11 +19,12 @@ from ._binding import (  # noqa: F401
     release,
     reserve,
     status_string,
+    topk_plan,
     workspace_bytes,
     workspace_size,
 )
 
 __all__ = ["mla_sparse_decode", "mla_sparse_decode_noalloc", "mla_sparse_gather_dequant", "mla_kv_append",
-           "mla_topk_select", "plan", "prepare",
+           "mla_topk_select", "topk_plan", "plan", "prepare",
            "reserve", "release", "workspace_bytes", "workspace_size", "describe", "Tensor",
            "load_library", "library_path", "status_string", "MlasdError"]

@@ -65,13 +65,15 @@ def load_library():
     lib.mla_sparse_gather_dequant.argtypes = [T, T, T, T, T, T, vp]
     lib.mla_kv_append.argtypes = [T, T, T, T, T, vp]
     lib.mla_topk_select.argtypes = [T, T, T, vp]
+    lib.mla_topk_select_ex.argtypes = [T, T, T, i32, vp]
+    lib.mla_topk_plan.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(sz)]
     lib.mlasd_prepare.argtypes = [vp, i32, i32]
     lib.mlasd_reserve.argtypes = [vp, sz]
     lib.mlasd_release.argtypes = [vp]
     lib.mlasd_workspace_bytes.argtypes = [vp, ctypes.POINTER(sz)]
     for name in ("mla_sparse_decode", "mla_sparse_decode_ex", "mla_sparse_decode_noalloc", "mla_sparse_plan",
                  "mla_sparse_workspace_size", "mla_sparse_gather_dequant", "mla_kv_append", "mla_topk_select",
-                 "mlasd_prepare", "mlasd_reserve", "mlasd_release", "mlasd_workspace_bytes"):
+                 "mla_topk_select_ex", "mla_topk_plan", "mlasd_prepare", "mlasd_reserve", "mlasd_release", "mlasd_workspace_bytes"):
         getattr(lib, name).restype = ctypes.c_int
     lib.mlasd_status_string.argtypes = [ctypes.c_int]
     lib.mlasd_status_string.restype = ctypes.c_char_p
@@ -265,10 +267,13 @@ def mla_kv_append(latent, seq_ids, positions, page_table, kv_pages, stream=None)
     return kv_pages
 
 
-def mla_topk_select(scores, seq_lens, k=MAX_TOPK, out=None, stream=None):
+def mla_topk_select(scores, seq_lens, k=MAX_TOPK, out=None, stream=None, parts=None):
     """Each query's top-k positions from its indexer scores (fp32 [B,
     max_len]; candidates 0 .. min(seq_len, max_len) - 1): int32 [B, k] in
-    rank order (higher score first, ties by lower position), -1 padded."""
+    rank order (higher score first, ties by lower position), -1 padded.
+    `parts` forces the workgroups per long row of the candidate pass (None:
+    library plan, which cuts rows only when the stream's scratch holds
+    topk_plan's bytes; a forced split needs them reserved)."""
     dev = _same_device(scores, seq_lens)
     B = scores.shape[0] if scores.dim() == 2 else -1
     if out is None:
@@ -277,6 +282,19 @@ def mla_topk_select(scores, seq_lens, k=MAX_TOPK, out=None, stream=None):
     lib = load_library()
     descs = [describe(t) for t in (scores, seq_lens, out)]
     with torch.cuda.device(dev):
-        rc = lib.mla_topk_select(*[ctypes.byref(d) for d in descs], _stream(stream, dev))
+        args = [ctypes.byref(d) for d in descs]
+        if parts is None:
+            rc = lib.mla_topk_select(*args, _stream(stream, dev))
+        else:
+            rc = lib.mla_topk_select_ex(*args, int(parts), _stream(stream, dev))
     _check(rc, "mla_topk_select")
     return out
+
+
+def topk_plan(batch: int, max_len: int, parts: int = 0, num_cus: int = 0):
+    """(parts per row, bytes of split scratch) of a top-k selection over
+    [batch, max_len] scores."""
+    lib = load_library()
+    a, n = ctypes.c_int32(0), ctypes.c_size_t(0)
+    _check(lib.mla_topk_plan(batch, max_len, parts, num_cus, ctypes.byref(a), ctypes.byref(n)), "mla_topk_plan")
+    return a.value, n.value

@@ -4,6 +4,7 @@
 // mlasd_release.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <map>
@@ -365,6 +366,75 @@ int decode_impl(const mlasd_tensor* q, const mlasd_tensor* kv, const mlasd_tenso
   return launch_decode_call(call, ws, ws_bytes, stream);
 }
 
+// Top-k plan: when every row can have at least kTopkMinParts compute units,
+// rows of max_len >= kTopkMinParts * kTopkPartLen positions are cut into
+// parts of at least kTopkPartLen positions, one workgroup each, for the
+// candidate pass (a pass over a row is bound by the loads one workgroup
+// keeps in flight); one workgroup per row then selects and sorts.  The
+// second launch, the sampled threshold every part repeats and the join
+// cost about as much as two parts save: on 256 CUs 2 parts measured slower
+// than one workgroup per row at every shape tried, 4 and 8 faster.
+constexpr int kTopkMaxParts = 8;
+constexpr int kTopkMinParts = 4;
+constexpr int kTopkPartLen = 16384;
+
+int topk_parts(int32_t batch, int32_t max_len, int cus) {
+  if (batch <= 0) return 1;
+  const int parts = std::min({kTopkMaxParts, cus / batch, max_len / kTopkPartLen});
+  return parts >= kTopkMinParts ? parts : 1;
+}
+
+int topk_impl(const mlasd_tensor* scores, const mlasd_tensor* seq_lens, const mlasd_tensor* topk_idx,
+              int32_t parts_request, hipStream_t stream) {
+  if (scores == nullptr || topk_idx == nullptr) return MLASD_ERR_NULL;
+  if (scores->ndim != 2 || scores->shape[0] < 0 || scores->shape[0] > INT32_MAX || scores->shape[1] > INT32_MAX)
+    return MLASD_ERR_SHAPE;
+  const int64_t B = scores->shape[0];
+  const int64_t wsc[2] = {B, -1};
+  int rc = check_tensor(scores, MLASD_F32, 2, wsc, true);
+  if (rc != MLASD_OK) return rc;
+  const int64_t wl[1] = {B};
+  rc = check_tensor(seq_lens, MLASD_I32, 1, wl, true, false);
+  if (rc != MLASD_OK) return rc;
+  if (topk_idx->ndim != 2 || topk_idx->shape[1] < 0 || topk_idx->shape[1] > MLASD_MAX_TOPK) return MLASD_ERR_SHAPE;
+  const int64_t wi[2] = {B, -1};
+  rc = check_tensor(topk_idx, MLASD_I32, 2, wi, true);
+  if (rc != MLASD_OK) return rc;
+  if (parts_request > kTopkMaxParts) return MLASD_ERR_SHAPE;
+  if (B == 0 || topk_idx->shape[1] == 0) return MLASD_OK;
+  if (!aligned(scores->data, 4) || !aligned(seq_lens->data, 4) || !aligned(topk_idx->data, 4)) return MLASD_ERR_ALIGN;
+  int cus = 0;
+  rc = device_cus(&cus);
+  if (rc != MLASD_OK) return rc;
+  mlasd::TopkParams p{};
+  p.scores = (const float*)scores->data;
+  p.sc_sb = scores->stride[0];
+  p.max_len = (int32_t)scores->shape[1];
+  p.seq_lens = (const int32_t*)seq_lens->data;
+  p.len_s = seq_lens->stride[0];
+  p.batch = (int32_t)B;
+  p.topk_idx = (int32_t*)topk_idx->data;
+  p.idx_sb = topk_idx->stride[0];
+  p.k = (int32_t)topk_idx->shape[1];
+  p.parts = parts_request > 0 ? parts_request : topk_parts(p.batch, p.max_len, cus);
+  void* ws = nullptr;
+  if (p.parts > 1) {
+    int dev = 0;
+    rc = current_device(&dev);
+    if (rc != MLASD_OK) return rc;
+    size_t ws_bytes = 0;
+    lookup_workspace(dev, stream, &ws, &ws_bytes);
+    if (ws == nullptr || ws_bytes < mlasd::topk_workspace_bytes(p.batch, p.parts)) {
+      if (parts_request > 0) return MLASD_ERR_WORKSPACE;
+      p.parts = 1;   // automatic plan without the stream's scratch: one workgroup per row
+      ws = nullptr;
+    }
+  }
+  hipError_t e = mlasd::launch_topk(p, ws, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return MLASD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -528,37 +598,25 @@ int mla_kv_append(const mlasd_tensor* latent, const mlasd_tensor* seq_ids, const
 
 int mla_topk_select(const mlasd_tensor* scores, const mlasd_tensor* seq_lens, const mlasd_tensor* topk_idx,
                     mlasd_stream_t stream) {
-  if (scores == nullptr || topk_idx == nullptr) return MLASD_ERR_NULL;
-  if (scores->ndim != 2 || scores->shape[0] < 0 || scores->shape[0] > INT32_MAX || scores->shape[1] > INT32_MAX)
-    return MLASD_ERR_SHAPE;
-  const int64_t B = scores->shape[0];
-  const int64_t wsc[2] = {B, -1};
-  int rc = check_tensor(scores, MLASD_F32, 2, wsc, true);
-  if (rc != MLASD_OK) return rc;
-  const int64_t wl[1] = {B};
-  rc = check_tensor(seq_lens, MLASD_I32, 1, wl, true, false);
-  if (rc != MLASD_OK) return rc;
-  if (topk_idx->ndim != 2 || topk_idx->shape[1] < 0 || topk_idx->shape[1] > MLASD_MAX_TOPK) return MLASD_ERR_SHAPE;
-  const int64_t wi[2] = {B, -1};
-  rc = check_tensor(topk_idx, MLASD_I32, 2, wi, true);
-  if (rc != MLASD_OK) return rc;
-  if (B == 0 || topk_idx->shape[1] == 0) return MLASD_OK;
-  if (!aligned(scores->data, 4) || !aligned(seq_lens->data, 4) || !aligned(topk_idx->data, 4)) return MLASD_ERR_ALIGN;
-  int cus = 0;
-  rc = device_cus(&cus);
-  if (rc != MLASD_OK) return rc;
-  mlasd::TopkParams p{};
-  p.scores = (const float*)scores->data;
-  p.sc_sb = scores->stride[0];
-  p.max_len = (int32_t)scores->shape[1];
-  p.seq_lens = (const int32_t*)seq_lens->data;
-  p.len_s = seq_lens->stride[0];
-  p.batch = (int32_t)B;
-  p.topk_idx = (int32_t*)topk_idx->data;
-  p.idx_sb = topk_idx->stride[0];
-  p.k = (int32_t)topk_idx->shape[1];
-  hipError_t e = mlasd::launch_topk(p, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e);
+  return topk_impl(scores, seq_lens, topk_idx, 0, (hipStream_t)stream);
+}
+
+int mla_topk_select_ex(const mlasd_tensor* scores, const mlasd_tensor* seq_lens, const mlasd_tensor* topk_idx,
+                       int32_t parts, mlasd_stream_t stream) {
+  return topk_impl(scores, seq_lens, topk_idx, parts, (hipStream_t)stream);
+}
+
+int mla_topk_plan(int32_t batch, int32_t max_len, int32_t parts_request, int32_t num_cus, int32_t* parts,
+                  size_t* bytes) {
+  if (!parts || !bytes) return MLASD_ERR_NULL;
+  if (batch < 0 || max_len < 0 || parts_request > kTopkMaxParts) return MLASD_ERR_SHAPE;
+  int cus = num_cus;
+  if (cus <= 0 && parts_request <= 0) {
+    int rc = device_cus(&cus);
+    if (rc != MLASD_OK) return rc;
+  }
+  *parts = parts_request > 0 ? parts_request : topk_parts(batch, max_len, cus);
+  *bytes = mlasd::topk_workspace_bytes(batch, *parts);
   return MLASD_OK;
 }
 

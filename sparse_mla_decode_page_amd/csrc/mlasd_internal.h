@@ -99,6 +99,10 @@ struct TopkParams {
   int32_t* topk_idx;          // [B, k], innermost contiguous
   int64_t idx_sb;
   int32_t k;                  // 1 .. 512
+  int32_t parts;              // workgroups per long row in the candidate pass (1 .. 8)
+  int32_t cap_part;           // composites per part's list (set by launch_topk)
+  uint64_t* ws_list;          // [B, parts, cap_part] part lists  (parts > 1)
+  uint32_t* ws_cnt;           // [B, parts] part counts
 };
 
 // Split scratch of the entry point that allocates nothing: a static device
@@ -112,6 +116,9 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_combine(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_gather(const GatherParams& p, hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
-hipError_t launch_topk(const TopkParams& p, hipStream_t stream);
+// Bytes of workspace a top-k launch of `parts` parts per row needs (0 for 1).
+size_t topk_workspace_bytes(int32_t batch, int32_t parts);
+// ws: topk_workspace_bytes(p.batch, p.parts) bytes, 8-byte aligned (unused for parts 1).
+hipError_t launch_topk(TopkParams p, void* ws, hipStream_t stream);
 
 }  // namespace mlasd

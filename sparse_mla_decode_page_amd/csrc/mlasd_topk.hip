@@ -48,6 +48,7 @@ constexpr int kSmallRow = 4096;    // rows up to this length go to the list whol
 constexpr int kSample = kTopkThreads;
 constexpr int kUnroll = 8;         // float4 loads in flight per thread in a compaction pass
 constexpr int kSweepUnroll = 2;    // and in a histogram pass over the row (the rare path)
+constexpr int kMaxParts = 8;       // workgroups per row in the candidate pass, at most
 
 struct TopkSmem {
   uint64_t cand[kCand];
@@ -168,19 +169,21 @@ __device__ __forceinline__ uint32_t wave_reserve(uint32_t* count, uint32_t mine)
   return base + incl - mine;
 }
 
-// A row of L >= 1 positions: head [0, hh) before the first 16-byte
-// boundary, body of nv float4 vectors (positions hh + 4 j + e), tail
-// [hh + 4 nv, L).
+// L >= 1 consecutive positions of a row, the first at row position pos0:
+// head [0, hh) before the first 16-byte boundary, body of nv float4
+// vectors (elements hh + 4 j + e), tail [hh + 4 nv, L).  Composites and
+// takes see row positions, pos0 + element.
 struct RowView {
   const float* row;
   const f32x4* body;
-  int L, hh, nv;
+  int L, hh, nv, pos0;
 };
 
-__device__ __forceinline__ RowView view_row(const float* row, int L) {
+__device__ __forceinline__ RowView view_row(const float* row, int L, int pos0 = 0) {
   RowView rv;
   rv.row = row;
   rv.L = L;
+  rv.pos0 = pos0;
   rv.hh = min(L, (int)(((16u - (uint32_t)(reinterpret_cast<uintptr_t>(row) & 15u)) & 15u) >> 2));
   rv.body = reinterpret_cast<const f32x4*>(row + rv.hh);
   rv.nv = (L - rv.hh) >> 2;
@@ -192,9 +195,9 @@ __device__ __forceinline__ RowView view_row(const float* row, int L) {
 template <class F>
 __device__ __forceinline__ void for_singles(const RowView& rv, F&& f) {
   const int tid = threadIdx.x;
-  if (rv.hh > 0) f(tid < rv.hh, rv.row[min(tid, rv.hh - 1)], tid);   // uniform
+  if (rv.hh > 0) f(tid < rv.hh, rv.row[min(tid, rv.hh - 1)], rv.pos0 + tid);   // uniform
   const int t0 = rv.hh + 4 * rv.nv;
-  if (t0 < rv.L) f(t0 + tid < rv.L, rv.row[min(t0 + tid, rv.L - 1)], t0 + tid);   // uniform
+  if (t0 < rv.L) f(t0 + tid < rv.L, rv.row[min(t0 + tid, rv.L - 1)], rv.pos0 + t0 + tid);   // uniform
 }
 
 // Body vectors base + u * kTopkThreads + tid into x[u] (clamped to the last one); nv >= 1.
@@ -217,7 +220,8 @@ __device__ __forceinline__ void emit_batch(const RowView& rv, const f32x4 (&x)[k
   for (int u = 0; u < kUnroll; ++u) {
     const int j = base + u * kTopkThreads + tid;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) m |= (j < rv.nv && take(x[u][e], rv.hh + 4 * j + e)) ? 1ull << (4 * u + e) : 0ull;
+    for (int e = 0; e < 4; ++e)
+      m |= (j < rv.nv && take(x[u][e], rv.pos0 + rv.hh + 4 * j + e)) ? 1ull << (4 * u + e) : 0ull;
   }
   uint32_t slot = wave_reserve(count, (uint32_t)__popcll(m));
   // each lane walks its set bits (few: the takes are sparse), two at a
@@ -234,11 +238,11 @@ __device__ __forceinline__ void emit_batch(const RowView& rv, const f32x4 (&x)[k
     const float x0 = rv.row[h0 ? p0 : 0];
     const float x1 = rv.row[h1 ? p1 : 0];
     if (h0) {
-      if (slot < (uint32_t)cap) list[slot] = composite(x0, p0);
+      if (slot < (uint32_t)cap) list[slot] = composite(x0, rv.pos0 + p0);
       ++slot;
     }
     if (h1) {
-      if (slot < (uint32_t)cap) list[slot] = composite(x1, p1);
+      if (slot < (uint32_t)cap) list[slot] = composite(x1, rv.pos0 + p1);
       ++slot;
     }
   }
@@ -282,7 +286,7 @@ __device__ __forceinline__ void sweep_row(const RowView& rv, F&& f) {
     for (int u = 0; u < kSweepUnroll; ++u) {
       const int j = base + u * kTopkThreads + tid;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) f(j < rv.nv, composite(x[u][e], rv.hh + 4 * j + e));
+      for (int e = 0; e < 4; ++e) f(j < rv.nv, composite(x[u][e], rv.pos0 + rv.hh + 4 * j + e));
     }
   }
   for_singles(rv, [&](bool ok, float x, int pos) { f(ok, composite(x, pos)); });
@@ -342,9 +346,64 @@ __device__ __forceinline__ uint32_t sample_rank(int L, int k) {
   return (uint32_t)min(kSample, max(8, (int)((3ll * k * kSample + L - 1) / L)));
 }
 
-// Steps 1-3 for one row: the min(k, L) picks appended to sm.sel.
+// Step 1 for a row of L > kSmallRow positions: t0 from the sample of
+// kSample positions spread over the whole row (every workgroup of a row
+// that is cut into parts computes the same t0).
+__device__ __forceinline__ uint64_t row_threshold(TopkSmem& sm, const float* row, int L, int k) {
+  const int sp = (int)(((int64_t)threadIdx.x * L) / kSample);
+  const uint64_t sc = composite(row[sp], sp);
+  return radix_threshold(sm, sample_rank(L, k), 2, [&](auto&& f) { f(true, sc); });
+}
+
+// Step 2 over the positions of rv: appends their composites >= t0 to
+// list[0 .. cap), counting in *count (past cap: counted, not stored).
+// t0's low 42 bits are 0, so composite >= t0 is key >= kt.  Below
+// key(-inf) every position qualifies: all of rv is appended, or only
+// counted if it cannot fit.  Otherwise kt is the key of a float f0; when f0
+// is normal or infinite, key(x) >= kt is x >= f0 in float order (NaN is
+// below f0 on both sides, -0 equals +0, and a denormal x lies on the same
+// side of f0 whether flushed or not).  x0 holds rv's first body batch.
+__device__ __forceinline__ void compact_above(const RowView& rv, const f32x4 (&x0)[kUnroll], uint64_t t0,
+                                              uint64_t* list, uint32_t* count, int cap) {
+  const uint32_t kt = (uint32_t)(t0 >> 32);
+  const uint32_t fb = kt >= 0x80000000u ? kt ^ 0x80000000u : ~kt;
+  if (kt <= 0x007FFFFFu) {
+    if (rv.L <= cap)
+      compact_row(rv, x0, [](float, int) { return true; }, list, count, cap);
+    else if (threadIdx.x == 0)
+      *count = (uint32_t)rv.L;
+  } else if ((fb & 0x7F800000u) != 0) {
+    const float f0 = __uint_as_float(fb);
+    compact_row(rv, x0, [f0](float x, int) { return x >= f0; }, list, count, cap);
+  } else {
+    compact_row(rv, x0, [kt](float x, int) { return score_key(x) >= kt; }, list, count, cap);
+  }
+}
+
+// Step 3 with the candidate list in sm.cand[0 .. sm.n_cand) (n_cand past
+// kCand: the list overflowed): the k picks appended to sm.sel.  Called by
+// every thread after a barrier that follows the list's last write.
+__device__ __forceinline__ void select_picks(TopkSmem& sm, const RowView& rv, int k) {
+  const uint32_t nc = sm.n_cand;
+  if (nc >= (uint32_t)k && nc <= (uint32_t)kCand) {
+    const uint64_t tc = radix_threshold(sm, (uint32_t)k, 6, [&](auto&& f) { sweep_list(sm.cand, (int)nc, f); });
+    sweep_list(sm.cand, (int)nc, [&](bool ok, uint64_t c) {
+      const bool take = ok && c >= tc;
+      const uint32_t slot = wave_reserve(&sm.n_sel, take ? 1u : 0u);
+      if (take && slot < (uint32_t)kMaxTopk) sm.sel[slot] = c;
+    });
+  } else {   // the guess left too few or too many: select over the row
+    const uint64_t tc = radix_threshold(sm, (uint32_t)k, 6, [&](auto&& f) { sweep_row(rv, f); });
+    f32x4 x0[kUnroll];
+    if (rv.nv > 0) load_batch(rv, 0, x0);
+    compact_row(rv, x0, [tc](float x, int pos) { return composite(x, pos) >= tc; }, sm.sel, &sm.n_sel, kMaxTopk);
+  }
+  __syncthreads();
+}
+
+// Steps 1-3 for one row in one workgroup: the min(k, L) picks appended to sm.sel.
 __device__ __forceinline__ void select_row(TopkSmem& sm, const RowView& rv, int k) {
-  const int tid = threadIdx.x, L = rv.L;
+  const int L = rv.L;
   // the body's first batch is requested before the sample's select runs
   f32x4 x0[kUnroll];
   if (rv.nv > 0) load_batch(rv, 0, x0);
@@ -356,46 +415,11 @@ __device__ __forceinline__ void select_row(TopkSmem& sm, const RowView& rv, int 
   if (L <= kSmallRow) {   // the whole row is the list
     compact_row(rv, x0, [](float, int) { return true; }, sm.cand, &sm.n_cand, kCand);
   } else {
-    // 1. the sample: kSample positions spread over the row
-    const int sp = (int)(((int64_t)tid * L) / kSample);
-    const uint64_t sc = composite(rv.row[sp], sp);
-    const uint64_t t0 = radix_threshold(sm, sample_rank(L, k), 2, [&](auto&& f) { f(true, sc); });
-    // 2. the list: t0's low 42 bits are 0, so composite >= t0 is key >=
-    // kt.  Below key(-inf) every position qualifies: the whole row is the
-    // list, or overflows it.  Otherwise kt is the key of a float f0; when f0 is normal
-    // or infinite, key(x) >= kt is x >= f0 in float order (NaN is below f0
-    // on both sides, -0 equals +0, and a denormal x lies on the same side
-    // of f0 whether flushed or not).
-    const uint32_t kt = (uint32_t)(t0 >> 32);
-    const uint32_t fb = kt >= 0x80000000u ? kt ^ 0x80000000u : ~kt;
-    if (kt <= 0x007FFFFFu) {
-      if (L <= kCand)
-        compact_row(rv, x0, [](float, int) { return true; }, sm.cand, &sm.n_cand, kCand);
-      else if (tid == 0)
-        sm.n_cand = (uint32_t)L;
-    } else if ((fb & 0x7F800000u) != 0) {
-      const float f0 = __uint_as_float(fb);
-      compact_row(rv, x0, [f0](float x, int) { return x >= f0; }, sm.cand, &sm.n_cand, kCand);
-    } else {
-      compact_row(rv, x0, [kt](float x, int) { return score_key(x) >= kt; }, sm.cand, &sm.n_cand, kCand);
-    }
+    const uint64_t t0 = row_threshold(sm, rv.row, L, k);
+    compact_above(rv, x0, t0, sm.cand, &sm.n_cand, kCand);
   }
   __syncthreads();
-  const uint32_t nc = sm.n_cand;
-  // 3. select and collect
-  if (nc >= (uint32_t)k && nc <= (uint32_t)kCand) {
-    const uint64_t tc = radix_threshold(sm, (uint32_t)k, 6, [&](auto&& f) { sweep_list(sm.cand, (int)nc, f); });
-    sweep_list(sm.cand, (int)nc, [&](bool ok, uint64_t c) {
-      const bool take = ok && c >= tc;
-      const uint32_t slot = wave_reserve(&sm.n_sel, take ? 1u : 0u);
-      if (take && slot < (uint32_t)kMaxTopk) sm.sel[slot] = c;
-    });
-  } else {
-    const uint64_t tc = radix_threshold(sm, (uint32_t)k, 6, [&](auto&& f) { sweep_row(rv, f); });
-    if (rv.nv > 0) load_batch(rv, 0, x0);
-    compact_row(rv, x0, [tc](float x, int pos) { return composite(x, pos) >= tc; }, sm.sel, &sm.n_sel, kMaxTopk);
-  }
-  __syncthreads();
+  select_picks(sm, rv, k);
 }
 
 // v of lane (lane ^ kS), kS < 64, within the wave
@@ -451,6 +475,42 @@ __device__ __forceinline__ void bitonic_from(uint64_t& v, uint64_t* buf0, uint64
     bitonic_from<kSize * 2, kSize, kNext>(v, buf0, buf1);
 }
 
+// A row of L positions that is cut into parts (L > k and L > kSmallRow):
+// part i covers [i c, min(L, (i + 1) c)), c = ceil(L / parts) rounded up
+// to a multiple of 4.
+__device__ __forceinline__ bool row_in_parts(int L, int k) { return L > k && L > kSmallRow; }
+__device__ __forceinline__ int part_len(int L, int parts) { return ((L + parts - 1) / parts + 3) & ~3; }
+
+// Rows cut into parts, one workgroup per (part, row): steps 1-2 over the
+// part, with the row's t0, into the part's region of the workspace.  Its
+// count (past cap_part: overflowed, nothing usable) goes to ws_cnt.
+__global__ __launch_bounds__(kTopkThreads, 1) void mla_topk_parts_kernel(const TopkParams p) {
+  __shared__ TopkSmem sm;
+  const int b = blockIdx.x % p.batch, part = blockIdx.x / p.batch, tid = threadIdx.x;
+  const int L = min(max(p.seq_lens[(int64_t)b * p.len_s], 0), p.max_len);
+  if (!row_in_parts(L, p.k)) return;   // the row is selected whole by mla_topk_kernel
+  const float* row = p.scores + (int64_t)b * p.sc_sb;
+  const int c = part_len(L, p.parts);
+  const int lo = min(L, part * c), n = min(L, lo + c) - lo;
+  uint32_t* cnt = p.ws_cnt + (int64_t)b * p.parts + part;
+  if (n == 0) {
+    if (tid == 0) *cnt = 0;
+    return;
+  }
+  for (int i = tid; i < kBins; i += kTopkThreads) sm.hist[i] = 0;
+  if (tid == 0) sm.n_cand = 0;
+  const RowView rv = view_row(row + lo, n, lo);
+  f32x4 x0[kUnroll];
+  if (rv.nv > 0) load_batch(rv, 0, x0);
+  __syncthreads();
+  const uint64_t t0 = row_threshold(sm, row, L, p.k);
+  compact_above(rv, x0, t0, p.ws_list + ((int64_t)b * p.parts + part) * p.cap_part, &sm.n_cand, p.cap_part);
+  __syncthreads();
+  if (tid == 0) *cnt = sm.n_cand;
+}
+
+// One workgroup per row: steps 1-3 (or, for a row cut into parts, the
+// parts' lists joined into the candidate list, then step 3), then step 4.
 __global__ __launch_bounds__(kTopkThreads, 1) void mla_topk_kernel(const TopkParams p) {
   __shared__ TopkSmem sm;
   const int b = blockIdx.x, tid = threadIdx.x;
@@ -466,7 +526,54 @@ __global__ __launch_bounds__(kTopkThreads, 1) void mla_topk_kernel(const TopkPar
     sm.n_sel = 0;
   }
   __syncthreads();
-  if (L > 0) select_row(sm, view_row(row, L), k);
+  if (p.parts > 1 && row_in_parts(L, k)) {
+    // the parts' counts, all requested at once (the same words for every
+    // thread); a part past its region, or a total the list cannot hold,
+    // sends step 3 to the row
+    const uint32_t* cnt = p.ws_cnt + (int64_t)b * p.parts;
+    uint32_t c[kMaxParts];
+#pragma unroll
+    for (int i = 0; i < kMaxParts; ++i) c[i] = i < p.parts ? cnt[i] : 0u;
+    // list entry f of the joined list is workspace entry f + gap[i] of the
+    // row's lists, i the part holding f: gap[i] = i * cap_part - (entries
+    // of the parts before i)
+    uint32_t total = 0, start[kMaxParts], gap[kMaxParts];
+    bool over = false;
+#pragma unroll
+    for (int i = 0; i < kMaxParts; ++i) {
+      start[i] = total;
+      gap[i] = (uint32_t)(i * p.cap_part) - total;
+      over |= c[i] > (uint32_t)p.cap_part;
+      total += c[i];
+    }
+    if (over || total > (uint32_t)kCand) {
+      total = kCand + 1;
+    } else if (total >= (uint32_t)k) {
+      const uint64_t* src = p.ws_list + (int64_t)b * p.parts * p.cap_part;
+      constexpr int kJ = 8;   // loads in flight per thread
+      for (uint32_t f0 = 0; f0 < total; f0 += kJ * kTopkThreads) {
+        uint64_t v[kJ];
+#pragma unroll
+        for (int u = 0; u < kJ; ++u) {
+          const uint32_t f = f0 + u * kTopkThreads + tid;
+          uint32_t g = 0;
+#pragma unroll
+          for (int i = 1; i < kMaxParts; ++i) g = (i < p.parts && f >= start[i]) ? gap[i] : g;
+          v[u] = src[f < total ? f + g : 0];
+        }
+#pragma unroll
+        for (int u = 0; u < kJ; ++u) {
+          const uint32_t f = f0 + u * kTopkThreads + tid;
+          if (f < total) sm.cand[f] = v[u];
+        }
+      }
+    }
+    if (tid == 0) sm.n_cand = total;
+    __syncthreads();
+    select_picks(sm, view_row(row, L), k);
+  } else if (L > 0) {
+    select_row(sm, view_row(row, L), k);
+  }
 
   // 4. sort the n picks (exactly n were appended) descending, thread i
   // holding entry i; entries past n hold 0, below every pick.  The
@@ -478,7 +585,21 @@ __global__ __launch_bounds__(kTopkThreads, 1) void mla_topk_kernel(const TopkPar
 
 }  // namespace
 
-hipError_t launch_topk(const TopkParams& p, hipStream_t stream) {
+size_t topk_workspace_bytes(int32_t batch, int32_t parts) {
+  if (parts <= 1) return 0;
+  const size_t cap = (size_t)(kCand / parts);
+  return (size_t)batch * parts * (cap * sizeof(uint64_t) + sizeof(uint32_t));
+}
+
+hipError_t launch_topk(TopkParams p, void* ws, hipStream_t stream) {
+  if (p.parts > 1) {
+    p.cap_part = kCand / p.parts;
+    p.ws_list = (uint64_t*)ws;
+    p.ws_cnt = (uint32_t*)(p.ws_list + (size_t)p.batch * p.parts * p.cap_part);
+    hipLaunchKernelGGL(mla_topk_parts_kernel, dim3(p.batch * p.parts), dim3(kTopkThreads), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(mla_topk_kernel, dim3(p.batch), dim3(kTopkThreads), 0, stream, p);
   return hipGetLastError();
 }

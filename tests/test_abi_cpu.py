@@ -332,3 +332,39 @@ def test_topk_select_validation_without_device():
     # empty work is a no-op
     assert _topk(lib, _t(0, F32, [0, 1000]), _t(0, I32, [0]), _t(0, I32, [0, 512])) == 0
     assert _topk(lib, ok["scores"], ok["lens"], _t(0x30000, I32, [4, 0])) == 0
+    # forced parts: more than 8 refused; the argument checks come first
+    r = ctypes.byref
+    ex = lib.mla_topk_select_ex
+    assert ex(r(ok["scores"]), r(ok["lens"]), r(ok["idx"]), 9, None) == -2
+    assert ex(None, r(ok["lens"]), r(ok["idx"]), 2, None) == -1
+    assert ex(r(_t(0x10000, I32, [4, 1000])), r(ok["lens"]), r(ok["idx"]), 2, None) == -2
+    assert ex(r(_t(0, F32, [0, 1000])), r(_t(0, I32, [0])), r(_t(0, I32, [0, 512])), 4, None) == 0
+
+
+@pytest.mark.parametrize("batch,max_len,req,cus,expect", [
+    (64, 65536, 0, 256, 4),     # the indexer's B=64 x 65,536: four workgroups per row
+    (1, 131072, 0, 256, 8),     # at most 8 parts
+    (16, 65536, 0, 256, 4),     # parts of at least 16,384 positions
+    (1, 65535, 0, 256, 1),      # fewer than 4 parts of 16,384: not cut
+    (128, 131072, 0, 256, 1),   # only 2 compute units per row: not cut
+    (64, 131072, 0, 256, 4),
+    (256, 131072, 0, 256, 1),   # every compute unit already has a row
+    (64, 32768, 0, 256, 1),
+    (0, 65536, 0, 256, 1),
+    (64, 65536, 8, 0, 8),       # forced: no device needed
+    (3, 100, 1, 0, 1),
+])
+def test_topk_plan(batch, max_len, req, cus, expect):
+    parts, nbytes = m.topk_plan(batch, max_len, req, cus)
+    assert parts == expect
+    # per row: the candidate list (16,384 composites of 8 bytes) shared by the parts, and a count per part
+    assert nbytes == (0 if parts == 1 else batch * parts * ((16384 // parts) * 8 + 4))
+
+
+def test_topk_plan_validation():
+    with pytest.raises(m.MlasdError):
+        m.topk_plan(4, 1000, 9, 256)
+    with pytest.raises(m.MlasdError):
+        m.topk_plan(-1, 1000, 0, 256)
+    with pytest.raises(m.MlasdError):
+        m.topk_plan(4, -1, 0, 256)

@@ -1,7 +1,8 @@
 """Top-k selection (the step before the decode) against the oracle, bit for
 bit: random and tie-heavy score rows, NaN / infinities / signed zeros, short,
 empty and clamped sequences, the full B=64 x 65,536 shape, and the selection
-chained before the decode in one captured graph."""
+chained before the decode in one captured graph -- each under the library's
+plan, one workgroup per row, and long rows cut into 3 or 8 parts."""
 import numpy as np
 import pytest
 import torch
@@ -14,20 +15,29 @@ from helpers import check_attention, reserve_for, to_device
 pytestmark = pytest.mark.gpu
 
 
-def _select(scores, lens, k):
+def _select(scores, lens, k, parts=None):
     s = torch.from_numpy(np.ascontiguousarray(scores)).cuda()
     l = torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda()
-    out = mlasd.mla_topk_select(s, l, k)
+    if parts is not None and parts > 1:
+        mlasd.reserve(mlasd.topk_plan(s.shape[0], s.shape[1], parts)[1])
+    out = mlasd.mla_topk_select(s, l, k, parts=parts)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
 
-def _check(scores, lens, k, label):
-    print(f"topk: {label} B={scores.shape[0]} max_len={scores.shape[1]} k={k}", flush=True)
-    got = _select(scores, lens, k)
+# None: the library's plan (a split only with enough scratch on the stream);
+# 1: one workgroup per row; 3 and 8: the candidate pass of rows longer than
+# max(k, 4096) cut into that many parts
+PARTS = (None, 1, 3, 8)
+
+
+def _check(scores, lens, k, label, parts=PARTS):
     ref = O.topk_select(scores, lens, k)
-    bad = np.argwhere(got != ref)
-    assert len(bad) == 0, f"{label}: {len(bad)} slots differ, first at {bad[:3].tolist()}"
+    for pa in parts:
+        print(f"topk: {label} B={scores.shape[0]} max_len={scores.shape[1]} k={k} parts={pa}", flush=True)
+        got = _select(scores, lens, k, pa)
+        bad = np.argwhere(got != ref)
+        assert len(bad) == 0, f"{label} parts={pa}: {len(bad)} slots differ, first at {bad[:3].tolist()}"
 
 
 @pytest.mark.parametrize("k", [1, 7, 100, 512])
@@ -50,10 +60,77 @@ def test_short_empty_and_clamped_lengths():
 
 
 def test_full_shape_b64_65536():
+    """The full shape under the library's plan with the scratch it asks for
+    (4 parts per row on 256 CUs), then forced plans."""
     sc = G.indexer_scores(15, 64, 65536)
     lens = np.full(64, 65536)
     lens[::7] = np.random.default_rng(15).integers(0, 65536, len(lens[::7]))
-    _check(sc, lens, 512, "B=64 x 65536")
+    parts, nbytes = mlasd.topk_plan(64, 65536)
+    if torch.cuda.get_device_properties(0).multi_processor_count >= 256:
+        assert parts == 4
+    mlasd.reserve(nbytes)
+    _check(sc, lens, 512, "B=64 x 65536", parts=(None, 1, 2, 8))
+
+
+def test_candidates_in_one_part():
+    """Rows whose large scores all sit in their first eighth: with 8 parts
+    one part's list overflows its share of the candidate list although the
+    row's total fits, and the selection falls back to the whole row; with 3
+    parts the same candidates fit.  Short rows in the batch are selected
+    whole."""
+    L = 65536
+    sc = G.indexer_scores(24, 4, L)
+    sc[:2, L // 8:] -= 100.0
+    sc[2, : 7 * L // 8] -= 100.0
+    _check(sc, [L, L - 5, L, 3000], 512, "candidates in one part", parts=(1, 3, 8))
+
+
+def test_forced_parts_need_scratch():
+    """A forced split on a stream without scratch is refused before anything
+    is enqueued; the library's plan there runs one workgroup per row."""
+    sc = torch.from_numpy(G.indexer_scores(25, 2, 65536)).cuda()
+    lens = torch.tensor([65536, 40000], dtype=torch.int32, device="cuda")
+    ref = O.topk_select(sc.cpu().numpy(), lens.cpu().numpy(), 512)
+    stream = torch.cuda.Stream()
+    out = torch.full((2, 512), -7, dtype=torch.int32, device="cuda")
+    with pytest.raises(mlasd.MlasdError) as ei:
+        mlasd.mla_topk_select(sc, lens, 512, out=out, stream=stream, parts=4)
+    assert ei.value.status == -8
+    stream.synchronize()
+    assert bool((out == -7).all())
+    got = mlasd.mla_topk_select(sc, lens, 512, stream=stream)
+    stream.synchronize()
+    assert np.array_equal(got.cpu().numpy(), ref)
+
+
+def test_split_selection_in_a_graph():
+    """The split selection (parts kernel, then the per-row kernel reading the
+    stream's scratch) captured in a graph and replayed with eager work and
+    new scores in between: every replay matches the oracle."""
+    B, L = 16, 65536
+    stream = torch.cuda.Stream()
+    parts, nbytes = mlasd.topk_plan(B, L, 4)
+    mlasd.reserve(nbytes, stream=stream)
+    sc = torch.empty((B, L), dtype=torch.float32, device="cuda")
+    lens_np = np.full(B, L)
+    lens_np[3] = 33000
+    lens_np[5] = 600
+    lens = torch.from_numpy(lens_np.astype(np.int32)).cuda()
+    idx = torch.empty((B, 512), dtype=torch.int32, device="cuda")
+    sc.copy_(torch.from_numpy(G.indexer_scores(26, B, L)))
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        mlasd.mla_topk_select(sc, lens, 512, out=idx, stream=stream, parts=parts)
+    for rep in range(3):
+        scores = G.indexer_scores(27 + rep, B, L)
+        sc.copy_(torch.from_numpy(scores))
+        idx.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(idx.cpu().numpy(), O.topk_select(scores, lens_np, 512)), f"replay {rep}"
+        torch.ones(1 << 20, device="cuda").sum()   # eager work between replays
 
 
 def test_full_length_ties():
