@@ -6,11 +6,11 @@
 // lower first (NaN ranks as -inf, -0.0 equals +0.0); the first min(k, L)
 // positions in rank order are written in that order, then -1.
 //
-// One workgroup per query.  Each candidate becomes a 64-bit composite,
-// (key << 32) | (2^32 - 1 - position), key a 32-bit map of the score whose
-// unsigned order is the score order: composites are distinct and their
-// unsigned order is the rank order, so the picks are exactly the min(k, L)
-// largest composites.
+// Steps 3-4 run in one workgroup per query.  Each candidate becomes a
+// 64-bit composite, (key << 32) | (2^32 - 1 - position), key a 32-bit map
+// of the score whose unsigned order is the score order: composites are
+// distinct and their unsigned order is the rank order, so the picks are
+// exactly the min(k, L) largest composites.
 //   1. Threshold guess (rows over kSmallRow positions): the composites of 512
 //      positions spread over the row; t0, the lower edge of the 22-bit bin
 //      holding their r-th largest, r set so about 3 k of the row's
@@ -29,6 +29,12 @@
 //   4. A bitonic sort of the <= 512 picks, descending, gives the output
 //      order: stages within a wave by DPP and lane swizzles, the six with
 //      strides of 64 and more through LDS.
+// At small batch, steps 1-2 of long rows can run in a launch of their own,
+// one workgroup per (part, row), each part of the row appending its
+// composites >= the row's t0 (the same sample, so the same t0 in every
+// part) to its own region of a workspace; the per-row launch then joins the
+// parts' lists in LDS and runs steps 3-4.  The picks, and so the output,
+// are the same as with one workgroup per row.
 // A row is read as a head of up to 3 positions before its first 16-byte
 // boundary, a body of float4 vectors and a tail of up to 3 positions.
 #include "mlasd_internal.h"
