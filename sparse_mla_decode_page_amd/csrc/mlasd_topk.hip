@@ -26,9 +26,10 @@
 //      k-th largest composite Tc, and the picks are the list's composites
 //      >= Tc.  Otherwise (guess too high or too low, e.g. long rows of
 //      equal scores) the same select and collection run over the row.
-//   4. A bitonic sort of the <= 512 picks, descending, gives the output
-//      order: stages within a wave by DPP and lane swizzles, the six with
-//      strides of 64 and more through LDS.
+//   4. Output order: each wave sorts its 64 of the <= 512 picks by
+//      bitonic stages within the wave (DPP and lane swizzles); a pick's
+//      place is the number of picks above it, its lane plus a binary search
+//      in each other wave's sorted run (composites are distinct).
 // At small batch, steps 1-2 of long rows can run in a launch of their own,
 // one workgroup per (part, row), each part of the row appending its
 // composites >= the row's t0 (the same sample, so the same t0 in every
@@ -48,6 +49,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTopkThreads = 512;
 constexpr int kTopkWaves = kTopkThreads / 64;
+static_assert(kTopkThreads == kMaxTopk, "one pick per thread in the output step");
 constexpr int kBins = 2048;
 constexpr int kCand = 16384;       // LDS candidate list (128 KiB)
 constexpr int kSmallRow = 4096;    // rows up to this length go to the list whole
@@ -446,39 +448,53 @@ __device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
   }
 }
 
-// One bitonic stage (kSize, kStride) over one composite per thread i:
-// pairs (i, i ^ kStride); segments of kSize alternate in direction so the
-// last stage leaves entries 0..511 descending.  Strides of 64 and more go
-// through LDS (buffer `buf`, one barrier), smaller ones stay in the wave.
+// One bitonic stage (kSize, kStride) over one composite per lane i of a
+// wave: pairs (i, i ^ kStride); segments of kSize alternate in direction,
+// so after the last stage (64, 1) the wave's 64 entries are descending.
 template <int kSize, int kStride>
-__device__ __forceinline__ void bitonic_stage(uint64_t& v, uint64_t* buf) {
-  const int i = threadIdx.x;
-  uint64_t o;
-  if constexpr (kStride >= 64) {
-    if (i < kMaxTopk) buf[i] = v;
-    __syncthreads();
-    o = i < kMaxTopk ? buf[i ^ kStride] : 0ull;
-  } else {
-    const uint32_t lo = lane_xor<kStride>((uint32_t)v);
-    const uint32_t hi = lane_xor<kStride>((uint32_t)(v >> 32));
-    o = ((uint64_t)hi << 32) | lo;
-  }
+__device__ __forceinline__ void wave_bitonic_stage(uint64_t& v) {
+  const int i = threadIdx.x & 63;
+  const uint32_t lo = lane_xor<kStride>((uint32_t)v);
+  const uint32_t hi = lane_xor<kStride>((uint32_t)(v >> 32));
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
   const bool keep_max = ((i & kStride) == 0) == ((i & kSize) == 0);
   const uint64_t mx = v > o ? v : o, mn = v > o ? o : v;
   v = keep_max ? mx : mn;
 }
 
-// Stages (kSize, kStride), (kSize, kStride / 2), .., then the next sizes up
-// to 512.  LDS stages alternate between two buffers, so each needs one
-// barrier: a buffer is written again only after a later barrier.
-template <int kSize, int kStride, int kLds>
-__device__ __forceinline__ void bitonic_from(uint64_t& v, uint64_t* buf0, uint64_t* buf1) {
-  bitonic_stage<kSize, kStride>(v, (kLds & 1) ? buf1 : buf0);
-  constexpr int kNext = kLds + (kStride >= 64 ? 1 : 0);
+// Stages (kSize, kStride), (kSize, kStride / 2), .., then the next sizes up to 64.
+template <int kSize, int kStride>
+__device__ __forceinline__ void wave_bitonic_from(uint64_t& v) {
+  wave_bitonic_stage<kSize, kStride>(v);
   if constexpr (kStride > 1)
-    bitonic_from<kSize, kStride / 2, kNext>(v, buf0, buf1);
-  else if constexpr (kSize < kMaxTopk)
-    bitonic_from<kSize * 2, kSize, kNext>(v, buf0, buf1);
+    wave_bitonic_from<kSize, kStride / 2>(v);
+  else if constexpr (kSize < 64)
+    wave_bitonic_from<kSize * 2, kSize>(v);
+}
+
+// Number of entries of run[0 .. 64), descending, above v: a binary search.
+__device__ __forceinline__ uint32_t count_above(const uint64_t* run, uint64_t v) {
+  uint32_t pos = 0;
+#pragma unroll
+  for (uint32_t st = 32; st >= 1; st >>= 1) pos += run[pos + st - 1] > v ? st : 0u;
+  return pos + (run[pos] > v ? 1u : 0u);
+}
+
+// 4. Thread i holds pick i (i < n) or 0 (below every pick).  The picks are
+// distinct, so each one's place in the output is the number of picks above
+// it: each wave sorts its 64 entries (its run), and a pick counts the
+// entries above it in every run by binary search (in its own run that is
+// its lane).  Picks go to dst[place]; places n .. k-1 get -1.
+__device__ __forceinline__ void write_ranked(uint64_t v, uint64_t* runs, int n, int k, int32_t* dst) {
+  const int tid = threadIdx.x;
+  wave_bitonic_from<2, 1>(v);
+  runs[tid] = v;
+  __syncthreads();
+  uint32_t place = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) place += count_above(runs + 64 * w, v);
+  if (v != 0) dst[place] = (int32_t)(0xFFFFFFFFu - (uint32_t)(v & 0xFFFFFFFFu));
+  if (tid >= n && tid < k) dst[tid] = -1;
 }
 
 // A row of L positions that is cut into parts (L > k and L > kSmallRow):
@@ -581,12 +597,9 @@ __global__ __launch_bounds__(kTopkThreads, 1) void mla_topk_kernel(const TopkPar
     select_row(sm, view_row(row, L), k);
   }
 
-  // 4. sort the n picks (exactly n were appended) descending, thread i
-  // holding entry i; entries past n hold 0, below every pick.  The
-  // candidate list is free by now and serves as the second LDS buffer.
-  uint64_t v = tid < n ? sm.sel[tid] : 0ull;
-  bitonic_from<2, 1, 0>(v, sm.cand, sm.sel);
-  if (tid < k) dst[tid] = tid < n ? (int32_t)(0xFFFFFFFFu - (uint32_t)(v & 0xFFFFFFFFu)) : -1;
+  // 4. the n picks (exactly n were appended) in rank order; the candidate
+  // list is free by now and holds the sorted runs
+  write_ranked(tid < n ? sm.sel[tid] : 0ull, sm.cand, n, k, dst);
 }
 
 }  // namespace
