@@ -102,7 +102,7 @@ struct TopkParams {
   int32_t parts;              // workgroups per long row in the candidate pass (1 .. 8)
   int32_t cap_part;           // composites per part's list (set by launch_topk)
   uint64_t* ws_list;          // [B, parts, cap_part] part lists  (parts > 1)
-  uint32_t* ws_cnt;           // [B, parts] part counts
+  uint64_t* ws_meta;          // [B, parts, 4] per part: count, t0, largest key, unused
 };
 
 // Split scratch of the entry point that allocates nothing: a static device

@@ -65,6 +65,7 @@ struct TopkSmem {
   uint32_t wave_tot[kTopkWaves];
   uint32_t found[3];   // digit, count above it, count in its bin
   uint32_t n_cand, n_sel;
+  uint32_t kmax;       // largest key appended to the candidate list
 };
 
 // Unsigned order of the key = rank order of the score.
@@ -220,7 +221,7 @@ __device__ __forceinline__ void load_batch(const RowView& rv, int base, f32x4 (&
 // The takes are kept as one bit each between the count and the writes.
 template <class Take>
 __device__ __forceinline__ void emit_batch(const RowView& rv, const f32x4 (&x)[kUnroll], int base, Take&& take,
-                                           uint64_t* list, uint32_t* count, int cap) {
+                                           uint64_t* list, uint32_t* count, int cap, uint32_t& mk) {
   static_assert(4 * kUnroll <= 64, "one bit per position of a batch");
   const int tid = threadIdx.x;
   uint64_t m = 0;
@@ -246,40 +247,65 @@ __device__ __forceinline__ void emit_batch(const RowView& rv, const f32x4 (&x)[k
     const float x0 = rv.row[h0 ? p0 : 0];
     const float x1 = rv.row[h1 ? p1 : 0];
     if (h0) {
-      if (slot < (uint32_t)cap) list[slot] = composite(x0, rv.pos0 + p0);
+      const uint64_t c = composite(x0, rv.pos0 + p0);
+      if (slot < (uint32_t)cap) list[slot] = c;
+      mk = max(mk, (uint32_t)(c >> 32));
       ++slot;
     }
     if (h1) {
-      if (slot < (uint32_t)cap) list[slot] = composite(x1, rv.pos0 + p1);
+      const uint64_t c = composite(x1, rv.pos0 + p1);
+      if (slot < (uint32_t)cap) list[slot] = c;
+      mk = max(mk, (uint32_t)(c >> 32));
       ++slot;
     }
   }
 }
 
+// Largest of x over lanes 0 .. i, in lane i (lane 63: the wave's largest):
+// the prefix pattern of wave_incl_sum with max in place of the sum.
+__device__ __forceinline__ uint32_t wave_incl_max(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, false));   // row_shr:1
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, false));   // row_shr:2
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, false));   // row_shr:4
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, false));   // row_shr:8
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false));   // row_bcast:15
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false));   // row_bcast:31
+  return x;
+}
+
 // Appends composite(x) of every position of the row with take(x,
-// position), in no particular order.  x0 holds the body's first batch.
+// position), in no particular order; if kmax is not null, the largest
+// appended key is max-ed into *kmax (LDS).  x0 holds the body's first
+// batch.
 template <class Take>
 __device__ __forceinline__ void compact_row(const RowView& rv, const f32x4 (&x0)[kUnroll], Take&& take,
-                                            uint64_t* list, uint32_t* count, int cap) {
+                                            uint64_t* list, uint32_t* count, int cap, uint32_t* kmax = nullptr) {
   constexpr int kStep = kUnroll * kTopkThreads;
+  uint32_t mk = 0;
   if (rv.nv > 0) {
     // two batches in flight: the next is requested before this one's appends
     f32x4 xa[kUnroll], xb[kUnroll];
     for (int u = 0; u < kUnroll; ++u) xa[u] = x0[u];
     for (int base = 0; base < rv.nv; base += 2 * kStep) {
       if (base + kStep < rv.nv) load_batch(rv, base + kStep, xb);   // uniform
-      emit_batch(rv, xa, base, take, list, count, cap);
+      emit_batch(rv, xa, base, take, list, count, cap, mk);
       if (base + kStep < rv.nv) {
         if (base + 2 * kStep < rv.nv) load_batch(rv, base + 2 * kStep, xa);
-        emit_batch(rv, xb, base + kStep, take, list, count, cap);
+        emit_batch(rv, xb, base + kStep, take, list, count, cap, mk);
       }
     }
   }
   for_singles(rv, [&](bool ok, float x, int pos) {
     const bool t = ok && take(x, pos);
     const uint32_t slot = wave_reserve(count, t ? 1u : 0u);
-    if (t && slot < (uint32_t)cap) list[slot] = composite(x, pos);
+    const uint64_t c = composite(x, pos);
+    if (t && slot < (uint32_t)cap) list[slot] = c;
+    if (t) mk = max(mk, (uint32_t)(c >> 32));
   });
+  if (kmax != nullptr) {   // uniform
+    mk = wave_incl_max(mk);
+    if ((threadIdx.x & 63) == 63 && mk != 0) atomicMax(kmax, mk);
+  }
 }
 
 // f(valid, composite) over the row's positions; every lane makes the same
@@ -348,6 +374,49 @@ __device__ __forceinline__ uint64_t radix_threshold(TopkSmem& sm, uint32_t need,
   return prefix << (64 - bits);
 }
 
+// Step 3's select over the candidate list sm.cand[0 .. nc), whose
+// composites all lie in [lo, hi]: the largest Tc with count(>= Tc) == need.
+// The first digit is (c >> s) - (lo >> s), s the least shift that fits
+// [lo, hi] into 2^11 bins, each bin the composites that share their top
+// 64 - s bits; then 11-bit digits below it (a last narrower one placed high
+// in a 10-bit histogram) until `need` takes a bin whole, which it does at
+// the latest when the bin holds one composite.  1 <= need <= nc; the
+// histogram is clear on entry and on exit.
+__device__ __forceinline__ uint64_t list_threshold(TopkSmem& sm, uint32_t need, uint64_t lo, uint64_t hi, int nc) {
+  // (hi - lo) >> s < 2^11, so (hi >> s) - (lo >> s) <= 2^11; one more bit if it is 2^11
+  int s = hi - lo < 2048u ? 0 : 53 - __builtin_clzll(hi - lo);
+  if ((hi >> s) - (lo >> s) > 2047u) ++s;
+  const uint64_t base = lo >> s;
+  sweep_list(sm.cand, nc, [&](bool ok, uint64_t c) {
+    hist_add(sm, (uint32_t)min((c >> s) - base, (uint64_t)2047u), ok);
+  });
+  __syncthreads();
+  uint32_t d, above, cnt;
+  find_digit<11>(sm, need, &d, &above, &cnt);
+  need -= above;
+  uint64_t prefix = base + d;
+  int bits = 64 - s;
+  while (cnt != need && bits < 64) {   // uniform
+    const int rem = 64 - bits;                 // 1 .. 63 bits below the prefix
+    const int used = rem < 11 ? rem : 11;
+    const int sh = rem - used;
+    const int pad = used < 10 ? 10 - used : 0;
+    sweep_list(sm.cand, nc, [&](bool ok, uint64_t c) {
+      const bool in = ok && (c >> rem) == prefix;
+      hist_add(sm, (uint32_t)((c >> sh) & ((1ull << used) - 1)) << pad, in);
+    });
+    __syncthreads();
+    if (used == 11)
+      find_digit<11>(sm, need, &d, &above, &cnt);
+    else
+      find_digit<10>(sm, need, &d, &above, &cnt);
+    need -= above;
+    prefix = (prefix << used) | (d >> pad);
+    bits += used;
+  }
+  return prefix << (64 - bits);
+}
+
 // r for a sample of kSample out of L > kSmallRow positions: about 3 k of the
 // row's composites lie at or above the sample's r-th largest.
 __device__ __forceinline__ uint32_t sample_rank(int L, int k) {
@@ -370,31 +439,34 @@ __device__ __forceinline__ uint64_t row_threshold(TopkSmem& sm, const float* row
 // counted if it cannot fit.  Otherwise kt is the key of a float f0; when f0
 // is normal or infinite, key(x) >= kt is x >= f0 in float order (NaN is
 // below f0 on both sides, -0 equals +0, and a denormal x lies on the same
-// side of f0 whether flushed or not).  x0 holds rv's first body batch.
+// side of f0 whether flushed or not).  The largest appended key is max-ed
+// into *kmax (LDS).  x0 holds rv's first body batch.
 __device__ __forceinline__ void compact_above(const RowView& rv, const f32x4 (&x0)[kUnroll], uint64_t t0,
-                                              uint64_t* list, uint32_t* count, int cap) {
+                                              uint64_t* list, uint32_t* count, int cap, uint32_t* kmax) {
   const uint32_t kt = (uint32_t)(t0 >> 32);
   const uint32_t fb = kt >= 0x80000000u ? kt ^ 0x80000000u : ~kt;
   if (kt <= 0x007FFFFFu) {
     if (rv.L <= cap)
-      compact_row(rv, x0, [](float, int) { return true; }, list, count, cap);
+      compact_row(rv, x0, [](float, int) { return true; }, list, count, cap, kmax);
     else if (threadIdx.x == 0)
       *count = (uint32_t)rv.L;
   } else if ((fb & 0x7F800000u) != 0) {
     const float f0 = __uint_as_float(fb);
-    compact_row(rv, x0, [f0](float x, int) { return x >= f0; }, list, count, cap);
+    compact_row(rv, x0, [f0](float x, int) { return x >= f0; }, list, count, cap, kmax);
   } else {
-    compact_row(rv, x0, [kt](float x, int) { return score_key(x) >= kt; }, list, count, cap);
+    compact_row(rv, x0, [kt](float x, int) { return score_key(x) >= kt; }, list, count, cap, kmax);
   }
 }
 
 // Step 3 with the candidate list in sm.cand[0 .. sm.n_cand) (n_cand past
-// kCand: the list overflowed): the k picks appended to sm.sel.  Called by
-// every thread after a barrier that follows the list's last write.
-__device__ __forceinline__ void select_picks(TopkSmem& sm, const RowView& rv, int k) {
+// kCand: the list overflowed), every composite of it at least lo and with
+// a key at most sm.kmax: the k picks appended to sm.sel.  Called by every
+// thread after a barrier that follows the list's last write.
+__device__ __forceinline__ void select_picks(TopkSmem& sm, const RowView& rv, int k, uint64_t lo) {
   const uint32_t nc = sm.n_cand;
   if (nc >= (uint32_t)k && nc <= (uint32_t)kCand) {
-    const uint64_t tc = radix_threshold(sm, (uint32_t)k, 6, [&](auto&& f) { sweep_list(sm.cand, (int)nc, f); });
+    const uint64_t hi = ((uint64_t)sm.kmax << 32) | 0xFFFFFFFFull;
+    const uint64_t tc = list_threshold(sm, (uint32_t)k, lo, hi, (int)nc);
     sweep_list(sm.cand, (int)nc, [&](bool ok, uint64_t c) {
       const bool take = ok && c >= tc;
       const uint32_t slot = wave_reserve(&sm.n_sel, take ? 1u : 0u);
@@ -420,14 +492,15 @@ __device__ __forceinline__ void select_row(TopkSmem& sm, const RowView& rv, int 
     __syncthreads();
     return;
   }
+  uint64_t t0 = 0;
   if (L <= kSmallRow) {   // the whole row is the list
-    compact_row(rv, x0, [](float, int) { return true; }, sm.cand, &sm.n_cand, kCand);
+    compact_row(rv, x0, [](float, int) { return true; }, sm.cand, &sm.n_cand, kCand, &sm.kmax);
   } else {
-    const uint64_t t0 = row_threshold(sm, rv.row, L, k);
-    compact_above(rv, x0, t0, sm.cand, &sm.n_cand, kCand);
+    t0 = row_threshold(sm, rv.row, L, k);
+    compact_above(rv, x0, t0, sm.cand, &sm.n_cand, kCand, &sm.kmax);
   }
   __syncthreads();
-  select_picks(sm, rv, k);
+  select_picks(sm, rv, k, t0);
 }
 
 // v of lane (lane ^ kS), kS < 64, within the wave
@@ -505,7 +578,8 @@ __device__ __forceinline__ int part_len(int L, int parts) { return ((L + parts -
 
 // Rows cut into parts, one workgroup per (part, row): steps 1-2 over the
 // part, with the row's t0, into the part's region of the workspace.  Its
-// count (past cap_part: overflowed, nothing usable) goes to ws_cnt.
+// record in ws_meta: the count (past cap_part: overflowed, nothing
+// usable), t0, and the largest key in its list.
 __global__ __launch_bounds__(kTopkThreads, 1) void mla_topk_parts_kernel(const TopkParams p) {
   __shared__ TopkSmem sm;
   const int b = blockIdx.x % p.batch, part = blockIdx.x / p.batch, tid = threadIdx.x;
@@ -514,21 +588,29 @@ __global__ __launch_bounds__(kTopkThreads, 1) void mla_topk_parts_kernel(const T
   const float* row = p.scores + (int64_t)b * p.sc_sb;
   const int c = part_len(L, p.parts);
   const int lo = min(L, part * c), n = min(L, lo + c) - lo;
-  uint32_t* cnt = p.ws_cnt + (int64_t)b * p.parts + part;
+  uint64_t* meta = p.ws_meta + ((int64_t)b * p.parts + part) * 4;
   if (n == 0) {
-    if (tid == 0) *cnt = 0;
+    if (tid == 0) meta[0] = meta[1] = meta[2] = 0;
     return;
   }
   for (int i = tid; i < kBins; i += kTopkThreads) sm.hist[i] = 0;
-  if (tid == 0) sm.n_cand = 0;
+  if (tid == 0) {
+    sm.n_cand = 0;
+    sm.kmax = 0;
+  }
   const RowView rv = view_row(row + lo, n, lo);
   f32x4 x0[kUnroll];
   if (rv.nv > 0) load_batch(rv, 0, x0);
   __syncthreads();
   const uint64_t t0 = row_threshold(sm, row, L, p.k);
-  compact_above(rv, x0, t0, p.ws_list + ((int64_t)b * p.parts + part) * p.cap_part, &sm.n_cand, p.cap_part);
+  compact_above(rv, x0, t0, p.ws_list + ((int64_t)b * p.parts + part) * p.cap_part, &sm.n_cand, p.cap_part,
+                &sm.kmax);
   __syncthreads();
-  if (tid == 0) *cnt = sm.n_cand;
+  if (tid == 0) {
+    meta[0] = sm.n_cand;
+    meta[1] = t0;
+    meta[2] = sm.kmax;
+  }
 }
 
 // One workgroup per row: steps 1-3 (or, for a row cut into parts, the
@@ -546,16 +628,21 @@ __global__ __launch_bounds__(kTopkThreads, 1) void mla_topk_kernel(const TopkPar
   if (tid == 0) {
     sm.n_cand = 0;
     sm.n_sel = 0;
+    sm.kmax = 0;
   }
   __syncthreads();
   if (p.parts > 1 && row_in_parts(L, k)) {
-    // the parts' counts, all requested at once (the same words for every
+    // the parts' records, all requested at once (the same words for every
     // thread); a part past its region, or a total the list cannot hold,
     // sends step 3 to the row
-    const uint32_t* cnt = p.ws_cnt + (int64_t)b * p.parts;
-    uint32_t c[kMaxParts];
+    const uint64_t* meta = p.ws_meta + (int64_t)b * p.parts * 4;
+    uint32_t c[kMaxParts], kmax = 0;
 #pragma unroll
-    for (int i = 0; i < kMaxParts; ++i) c[i] = i < p.parts ? cnt[i] : 0u;
+    for (int i = 0; i < kMaxParts; ++i) {
+      c[i] = i < p.parts ? (uint32_t)min(meta[4 * i], (uint64_t)0xFFFFFFFFu) : 0u;
+      kmax = max(kmax, i < p.parts ? (uint32_t)meta[4 * i + 2] : 0u);
+    }
+    const uint64_t t0 = meta[1];   // part 0 (never empty) holds the row's t0
     // list entry f of the joined list is workspace entry f + gap[i] of the
     // row's lists, i the part holding f: gap[i] = i * cap_part - (entries
     // of the parts before i)
@@ -590,9 +677,12 @@ __global__ __launch_bounds__(kTopkThreads, 1) void mla_topk_kernel(const TopkPar
         }
       }
     }
-    if (tid == 0) sm.n_cand = total;
+    if (tid == 0) {
+      sm.n_cand = total;
+      sm.kmax = kmax;
+    }
     __syncthreads();
-    select_picks(sm, view_row(row, L), k);
+    select_picks(sm, view_row(row, L), k, t0);
   } else if (L > 0) {
     select_row(sm, view_row(row, L), k);
   }
@@ -607,14 +697,14 @@ __global__ __launch_bounds__(kTopkThreads, 1) void mla_topk_kernel(const TopkPar
 size_t topk_workspace_bytes(int32_t batch, int32_t parts) {
   if (parts <= 1) return 0;
   const size_t cap = (size_t)(kCand / parts);
-  return (size_t)batch * parts * (cap * sizeof(uint64_t) + sizeof(uint32_t));
+  return (size_t)batch * parts * (cap + 4) * sizeof(uint64_t);
 }
 
 hipError_t launch_topk(TopkParams p, void* ws, hipStream_t stream) {
   if (p.parts > 1) {
     p.cap_part = kCand / p.parts;
     p.ws_list = (uint64_t*)ws;
-    p.ws_cnt = (uint32_t*)(p.ws_list + (size_t)p.batch * p.parts * p.cap_part);
+    p.ws_meta = p.ws_list + (size_t)p.batch * p.parts * p.cap_part;
     hipLaunchKernelGGL(mla_topk_parts_kernel, dim3(p.batch * p.parts), dim3(kTopkThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -357,8 +357,9 @@ def test_topk_select_validation_without_device():
 def test_topk_plan(batch, max_len, req, cus, expect):
     parts, nbytes = m.topk_plan(batch, max_len, req, cus)
     assert parts == expect
-    # per row: the candidate list (16,384 composites of 8 bytes) shared by the parts, and a count per part
-    assert nbytes == (0 if parts == 1 else batch * parts * ((16384 // parts) * 8 + 4))
+    # per row: the candidate list (16,384 composites of 8 bytes) shared by the parts, and a 32-byte
+    # record per part (count, threshold, largest composite)
+    assert nbytes == (0 if parts == 1 else batch * parts * ((16384 // parts) * 8 + 32))
 
 
 def test_topk_plan_validation():
