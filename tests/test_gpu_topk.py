@@ -72,6 +72,14 @@ def test_full_shape_b64_65536():
     _check(sc, lens, 512, "B=64 x 65536", parts=(None, 1, 2, 8))
 
 
+@pytest.mark.parametrize("k", [1, 7, 100])
+def test_long_rows_small_k(k):
+    """Long rows with a small k: the sampled threshold keeps few candidates
+    per part, and the joined list still holds the row's top k."""
+    sc = G.indexer_scores(28, 4, 100000)
+    _check(sc, [100000, 65536, 99999, 70001], k, f"long rows k={k}", parts=(None, 1, 4, 8))
+
+
 def test_candidates_in_one_part():
     """Rows whose large scores all sit in their first eighth: with 8 parts
     one part's list overflows its share of the candidate list although the
